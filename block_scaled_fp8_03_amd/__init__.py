@@ -1,0 +1,225 @@
+"""Block-scaled FP8 linear for AMD MI355X (gfx950): Python binding.
+
+This module only marshals torch tensors into the C ABI of ``libfp8bs.so``
+(declared in ``include/fp8bs.h``); every step of the computation runs in the
+library's HIP kernels.  PyTorch provides device memory and streams.
+
+Raw entry points carry the C names and take caller-allocated outputs:
+``fp8bs_act_quant``, ``fp8bs_weight_quant``, ``fp8bs_weight_dequant``,
+``fp8bs_gemm``, ``fp8bs_moe_gemm``.  Allocating conveniences: ``act_quant``,
+``weight_quant``, ``weight_dequant``, ``fp8_gemm``, ``moe_gemm``, ``linear``.
+
+The operations follow the DeepSeek-V3 inference pages ("DeepSeek-V3
+Administrator & Developer Guide", sections 6.3, 6.4, 8.5.1-8.5.3; "DeepSeek-V3
+User Guide", FAQ on scale_fmt ue8m0).  If the library has not been built the
+calls raise; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SCALE_FP32", "SCALE_UE8M0", "OUT_BF16", "OUT_F32", "Fp8bsError", "library_path", "lib",
+    "fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
+    "fp8bs_moe_gemm", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm",
+    "linear",
+]
+
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+BLOCK = 128
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
+_lib = None
+
+
+class Fp8bsError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int):
+        msg = lib().fp8bs_status_string(status).decode()
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libfp8bs.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is missing: build it with "
+                           "`python -m block_scaled_fp8_03_amd.build`")
+    L = ctypes.CDLL(library_path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.fp8bs_status_string.argtypes = [I]
+    L.fp8bs_status_string.restype = ctypes.c_char_p
+    L.fp8bs_version.restype = I
+    L.fp8bs_act_quant.argtypes = [P, P, P, I64, I64, I, P]
+    L.fp8bs_weight_quant.argtypes = [P, P, P, I64, I64, P]
+    L.fp8bs_weight_dequant.argtypes = [P, P, P, I64, I64, P]
+    L.fp8bs_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
+    L.fp8bs_moe_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, P]
+    for fn in ("fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
+               "fp8bs_moe_gemm"):
+        getattr(L, fn).restype = I
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- marshalling
+
+_F8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _need(t: torch.Tensor, dtypes, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _call(fn: str, *args) -> None:
+    st = getattr(lib(), fn)(*args)
+    if st != 0:
+        raise Fp8bsError(fn, st)
+
+
+def _fmt(scale_fmt) -> int:
+    if scale_fmt in (SCALE_FP32, "fp32", None):
+        return SCALE_FP32
+    if scale_fmt in (SCALE_UE8M0, "ue8m0"):
+        return SCALE_UE8M0
+    raise ValueError(f"unknown scale_fmt {scale_fmt!r}")
+
+
+def _out_code(c: torch.Tensor) -> int:
+    if c.dtype == torch.bfloat16:
+        return OUT_BF16
+    if c.dtype == torch.float32:
+        return OUT_F32
+    raise TypeError(f"output dtype {c.dtype} is neither bfloat16 nor float32")
+
+
+# ------------------------------------------------------- raw C-named wrappers
+
+def fp8bs_act_quant(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, scale_fmt=SCALE_FP32) -> None:
+    """x bf16 [M, K] -> q e4m3 [M, K], s float32 [M, K/128] (outputs preallocated)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    if tuple(q.shape) != (M, K) or tuple(s.shape) != (M, K // BLOCK if K % BLOCK == 0 else -1):
+        raise ValueError("q must be [M, K] and s [M, K/128]")
+    _call("fp8bs_act_quant", _need(x, (torch.bfloat16,), "x"), _need(q, _F8, "q"),
+          _need(s, (torch.float32,), "s"), M, K, _fmt(scale_fmt), _stream(x))
+
+
+def fp8bs_weight_quant(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor) -> None:
+    """w bf16 [N, K] -> q e4m3 [N, K], s float32 [ceil(N/128), ceil(K/128)]."""
+    N, K = w.shape
+    if tuple(q.shape) != (N, K) or tuple(s.shape) != (-(-N // BLOCK), -(-K // BLOCK)):
+        raise ValueError("q must be [N, K] and s [ceil(N/128), ceil(K/128)]")
+    _call("fp8bs_weight_quant", _need(w, (torch.bfloat16,), "w"), _need(q, _F8, "q"),
+          _need(s, (torch.float32,), "s"), N, K, _stream(w))
+
+
+def fp8bs_weight_dequant(w: torch.Tensor, s: torch.Tensor, y: torch.Tensor) -> None:
+    """w e4m3 [N, K], s float32 [ceil(N/128), ceil(K/128)] -> y bf16 [N, K]."""
+    N, K = w.shape
+    if tuple(s.shape) != (-(-N // BLOCK), -(-K // BLOCK)) or tuple(y.shape) != (N, K):
+        raise ValueError("s must be [ceil(N/128), ceil(K/128)] and y [N, K]")
+    _call("fp8bs_weight_dequant", _need(w, _F8, "w"), _need(s, (torch.float32,), "s"),
+          _need(y, (torch.bfloat16,), "y"), N, K, _stream(w))
+
+
+def fp8bs_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+               c: torch.Tensor) -> None:
+    """C [M, N] (bf16 or float32, by c.dtype) = block-scaled A [M, K] . B [N, K]^T."""
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2 or K % BLOCK:
+        raise ValueError("A and B need the same K, a multiple of 128")
+    if (tuple(a_s.shape) != (M, K // BLOCK) or tuple(b_s.shape) != (-(-N // BLOCK), K // BLOCK)
+            or tuple(c.shape) != (M, N)):
+        raise ValueError("scale or output shape mismatch")
+    _call("fp8bs_gemm", _need(a, _F8, "a"), _need(a_s, (torch.float32,), "a_s"),
+          _need(b, _F8, "b"), _need(b_s, (torch.float32,), "b_s"),
+          _need(c, (torch.bfloat16, torch.float32), "c"), M, N, K, _out_code(c), _stream(a))
+
+
+def fp8bs_moe_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                   offsets: torch.Tensor, c: torch.Tensor) -> None:
+    """Grouped GEMM: rows [offsets[e], offsets[e+1]) of A use expert e's B[e]."""
+    R, K = a.shape
+    E, N, K2 = b.shape
+    if K != K2 or K % BLOCK:
+        raise ValueError("A and B need the same K, a multiple of 128")
+    if (tuple(a_s.shape) != (R, K // BLOCK) or tuple(b_s.shape) != (E, -(-N // BLOCK), K // BLOCK)
+            or tuple(offsets.shape) != (E + 1,) or tuple(c.shape) != (R, N)):
+        raise ValueError("scale, offsets or output shape mismatch")
+    _call("fp8bs_moe_gemm", _need(a, _F8, "a"), _need(a_s, (torch.float32,), "a_s"),
+          _need(b, _F8, "b"), _need(b_s, (torch.float32,), "b_s"),
+          _need(offsets, (torch.int32,), "offsets"),
+          _need(c, (torch.bfloat16, torch.float32), "c"), R, E, N, K, _out_code(c), _stream(a))
+
+
+# ------------------------------------------------------ allocating wrappers
+
+def act_quant(x: torch.Tensor, scale_fmt="fp32"):
+    """x bf16 [..., K] -> (e4m3 [..., K], float32 [..., K/128])."""
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    q = torch.empty(x2.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((x2.shape[0], K // BLOCK), dtype=torch.float32, device=x.device)
+    fp8bs_act_quant(x2, q, s, scale_fmt)
+    return q.view(x.shape), s.view(*x.shape[:-1], K // BLOCK)
+
+
+def weight_quant(w: torch.Tensor):
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
+    s = torch.empty((-(-N // BLOCK), -(-K // BLOCK)), dtype=torch.float32, device=w.device)
+    fp8bs_weight_quant(w, q, s)
+    return q, s
+
+
+def weight_dequant(w: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    y = torch.empty(w.shape, dtype=torch.bfloat16, device=w.device)
+    fp8bs_weight_dequant(w, s, y)
+    return y
+
+
+def fp8_gemm(a, a_s, b, b_s, out_dtype=torch.bfloat16) -> torch.Tensor:
+    c = torch.empty((a.shape[0], b.shape[0]), dtype=out_dtype, device=a.device)
+    fp8bs_gemm(a, a_s, b, b_s, c)
+    return c
+
+
+def moe_gemm(a, a_s, b, b_s, offsets, out_dtype=torch.bfloat16) -> torch.Tensor:
+    c = torch.empty((a.shape[0], b.shape[1]), dtype=out_dtype, device=a.device)
+    fp8bs_moe_gemm(a, a_s, b, b_s, offsets, c)
+    return c
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, scale_fmt="fp32",
+           out_dtype=torch.bfloat16) -> torch.Tensor:
+    """The FP8 linear: act_quant(x) then the block-scaled GEMM with W (Admin
+    guide 6.3, gemm_impl = "fp8")."""
+    K = x.shape[-1]
+    q, s = act_quant(x.reshape(-1, K), scale_fmt)
+    y = fp8_gemm(q, s, w, w_s, out_dtype)
+    return y.view(*x.shape[:-1], w.shape[0])

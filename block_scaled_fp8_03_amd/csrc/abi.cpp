@@ -1,0 +1,152 @@
+// abi.cpp -- the C entry points declared in include/fp8bs.h.  Each one checks
+// its arguments on the host (no HIP call happens before the checks pass) and
+// then enqueues the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8bs.h"
+#include "launch.h"
+
+namespace {
+
+// The tile kernels address operands with 32-bit byte offsets and may touch up
+// to 256 rows past the end of an operand (those loads return zeros), so
+// (rows + 256) * K must stay below 2^32 for A and for (each expert's) B.
+constexpr int64_t kLimit32 = (int64_t)1 << 32;
+constexpr int64_t kLimitInt = ((int64_t)1 << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [p, p + n) and [q, q + m) intersect (empty ranges never do)
+bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
+  if (n <= 0 || m <= 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+// product of non-negative sizes, or -1 on int64 overflow
+int64_t mul(int64_t a, int64_t b) {
+  if (a == 0 || b == 0) return 0;
+  if (a > INT64_MAX / b) return -1;
+  return a * b;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bs_status_string(int status) {
+  switch (status) {
+    case FP8BS_OK: return "ok";
+    case FP8BS_ERR_NULL: return "a required pointer is NULL";
+    case FP8BS_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or size limit exceeded)";
+    case FP8BS_ERR_ALIGN: return "a pointer is not aligned as required (16 bytes for tensors, 4 for scales)";
+    case FP8BS_ERR_ENUM: return "unknown scale_fmt or out_dtype";
+    case FP8BS_ERR_HIP: return "HIP kernel launch failed";
+    case FP8BS_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    default: return "unknown status";
+  }
+}
+
+int fp8bs_version(void) { return 10000; }
+
+int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64_t K,
+                    int scale_fmt, void* stream) {
+  if (M < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (scale_fmt != FP8BS_SCALE_FP32 && scale_fmt != FP8BS_SCALE_UE8M0) return FP8BS_ERR_ENUM;
+  const int64_t n = mul(M, K);
+  if (n < 0 || mul(n, 2) < 0) return FP8BS_ERR_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (!x_bf16 || !q_e4m3 || !s) return FP8BS_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(s, 4)) return FP8BS_ERR_ALIGN;
+  const int64_t ns = n / 128;
+  if (overlap(q_e4m3, n, x_bf16, 2 * n) || overlap(s, 4 * ns, x_bf16, 2 * n) ||
+      overlap(q_e4m3, n, s, 4 * ns))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_act_quant(x_bf16, q_e4m3, s, M, K,
+                                           scale_fmt == FP8BS_SCALE_UE8M0, (hipStream_t)stream));
+}
+
+int fp8bs_weight_quant(const void* w_bf16, void* q_e4m3, float* s, int64_t N, int64_t K,
+                       void* stream) {
+  if (N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  const int64_t n = mul(N, K);
+  if (n < 0 || mul(n, 2) < 0 || cdiv(N, 128) > 65535 || cdiv(K, 128) > kLimitInt)
+    return FP8BS_ERR_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (!w_bf16 || !q_e4m3 || !s) return FP8BS_ERR_NULL;
+  if (!aligned(w_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(s, 4)) return FP8BS_ERR_ALIGN;
+  const int64_t ns = cdiv(N, 128) * cdiv(K, 128);
+  if (overlap(q_e4m3, n, w_bf16, 2 * n) || overlap(s, 4 * ns, w_bf16, 2 * n) ||
+      overlap(q_e4m3, n, s, 4 * ns))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_weight_quant(w_bf16, q_e4m3, s, N, K, (hipStream_t)stream));
+}
+
+int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64_t N, int64_t K,
+                         void* stream) {
+  if (N < 0 || K < 0) return FP8BS_ERR_SHAPE;
+  const int64_t n = mul(N, K);
+  if (n < 0 || mul(n, 2) < 0 || cdiv(N, 16) > 65535) return FP8BS_ERR_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (!w_e4m3 || !s || !y_bf16) return FP8BS_ERR_NULL;
+  if (!aligned(w_e4m3, 16) || !aligned(y_bf16, 16) || !aligned(s, 4)) return FP8BS_ERR_ALIGN;
+  const int64_t ns = cdiv(N, 128) * cdiv(K, 128);
+  if (overlap(y_bf16, 2 * n, w_e4m3, n) || overlap(y_bf16, 2 * n, s, 4 * ns)) return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_weight_dequant(w_e4m3, s, y_bf16, N, K, (hipStream_t)stream));
+}
+
+int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+               int64_t M, int64_t N, int64_t K, int out_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ENUM;
+  if (M > kLimitInt || N > kLimitInt || K > kLimitInt) return FP8BS_ERR_SHAPE;
+  const int64_t na = mul(M, K), nb = mul(N, K), nc = mul(M, N);
+  if (na < 0 || nb < 0 || nc < 0 || mul(M + 256, K) >= kLimit32 || mul(N + 256, K) >= kLimit32 ||
+      mul(nc, 4) < 0)
+    return FP8BS_ERR_SHAPE;
+  if (nc == 0) return FP8BS_OK;
+  if (!a || !a_s || !b || !b_s || !c) return FP8BS_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16) || !aligned(a_s, 4) ||
+      !aligned(b_s, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t cb = nc * (out_dtype == FP8BS_OUT_F32 ? 4 : 2);
+  const int64_t nas = M * (K / 128) * 4, nbs = cdiv(N, 128) * (K / 128) * 4;
+  if (overlap(c, cb, a, na) || overlap(c, cb, b, nb) || overlap(c, cb, a_s, nas) ||
+      overlap(c, cb, b_s, nbs))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_gemm(a, a_s, b, b_s, c, M, N, K, out_dtype == FP8BS_OUT_F32,
+                                      (hipStream_t)stream));
+}
+
+int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
+                   const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N, int64_t K,
+                   int out_dtype, void* stream) {
+  if (R < 0 || E < 0 || N < 0 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ENUM;
+  if (R > kLimitInt || E > kLimitInt || N > kLimitInt || K > kLimitInt) return FP8BS_ERR_SHAPE;
+  const int64_t na = mul(R, K), nbe = mul(N, K), nb = mul(E, nbe), nc = mul(R, N);
+  if (na < 0 || nbe < 0 || nb < 0 || nc < 0 || mul(R + 256, K) >= kLimit32 ||
+      mul(N + 256, K) >= kLimit32 || mul(nc, 4) < 0)
+    return FP8BS_ERR_SHAPE;
+  // the launch grid is (R / 64 + E) * ceil(N / 256) workgroups
+  if (mul(R / 64 + E, cdiv(N, 256)) > kLimitInt) return FP8BS_ERR_SHAPE;
+  if (nc == 0 || E == 0) return FP8BS_OK;
+  if (!a || !a_s || !b || !b_s || !offsets || !c) return FP8BS_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16) || !aligned(a_s, 4) ||
+      !aligned(b_s, 4) || !aligned(offsets, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t cb = nc * (out_dtype == FP8BS_OUT_F32 ? 4 : 2);
+  const int64_t nas = R * (K / 128) * 4, nbs = E * cdiv(N, 128) * (K / 128) * 4;
+  if (overlap(c, cb, a, na) || overlap(c, cb, b, nb) || overlap(c, cb, a_s, nas) ||
+      overlap(c, cb, b_s, nbs) || overlap(c, cb, offsets, 4 * (E + 1)))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_moe_gemm(a, a_s, b, b_s, offsets, c, R, E, N, K,
+                                          out_dtype == FP8BS_OUT_F32, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,536 @@
+// gemm.hip -- block-scaled FP8 GEMM kernels for gfx950 ("DeepSeek-V3
+// Administrator & Developer Guide" 8.5.3: an FP8 tiled matmul with a float32
+// accumulator, where each 128-wide K block's product is scaled by the row's
+// activation scale and the weight block's scale before being added), and the
+// grouped form used for the MoE experts (Admin guide 6.4).
+//
+// Orientation.  C = A . B^T with A [M, K] activations and B [N, K] weights.
+// The MFMA computes D[16 x 16] = X[16 x 128] . Y[128 x 16] with X taken from
+// the weights (rows = n) and Y from the activations (columns = m).  A lane
+// then holds four consecutive n of one m: those four share one weight scale,
+// so the scale applied to a lane's 16x16 partial is the single number
+// a_s[m, kb] * b_s[n/128, kb].
+//
+// MFMA operand layout (v_mfma_scale_f32_16x16x128_f8f6f4, fp8 e4m3 operands,
+// unit E8M0 scales): lane l supplies row (l % 16) of its operand and 32 of
+// the 128 K bytes, chosen by l / 16.  A K-block's dot product is the same
+// whichever 32 bytes each lane group carries, as long as both operands use
+// the same choice, so lane group g carries K bytes [32g, 32g + 32).  The
+// result lane l, register r is D[4 (l / 16) + r][l % 16].
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8bs {
+
+// One K = 128 FP8 MFMA with a zero accumulator (unit hardware scales: the
+// E8M0 value 127 is 2^0).
+__device__ __forceinline__ v4f mfma_k128(v8i x, v8i y) {
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, z, 0, 0, 0, 127, 0, 127);
+}
+
+// s_waitcnt that waits until at most n vector-memory operations of this wave
+// are outstanding (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their "no wait" maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses only (global memory traffic in
+// flight, e.g. prefetches, is not waited for).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 128-bit buffer resource for raw (untyped) loads of `bytes` bytes from
+// `base`; loads at offsets >= bytes return zeros instead of faulting.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;                                                   // 32-bit data format
+  return r;
+}
+
+// Direct buffer -> LDS loads: lane i's bytes land at LDS address
+// lds + size * i.  Written as inline assembly so the compiler does not treat
+// every later LDS read as dependent on every load in flight; completion is
+// tracked explicitly with wait_vmcnt() before the barrier that publishes a
+// stage.
+__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ----------------------------------------------------------------------------
+// Tile kernel
+// ----------------------------------------------------------------------------
+// A workgroup of 4 waves computes a BM x BN tile of C (BM rows of A, BN rows
+// of B); wave (wm, wn) computes a WM x WN sub-tile as (WN/16) x (WM/16) MFMA
+// tiles.  Each K block moves through a ring of ST LDS stages:
+//   stage = [A tile BM x 128 bytes][B tile BN x 128 bytes][a_s column, 256 floats]
+//           [b_s of each wave's weight block, 4 x 64 floats]
+// filled by direct buffer->LDS loads, so no VGPRs are spent on staging.
+// Rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+// position c ^ (r % 8), which spreads both the DMA writes (8 rows x 8 chunks
+// per wave instruction) and the MFMA operand reads (8 rows x one chunk per 8
+// lanes) over all LDS banks.  Rows past the end of an operand read as zeros
+// (buffer range check) and their results are never stored.
+
+struct GemmParams {
+  const uint8_t* a;       // [rows, K] e4m3
+  const float* a_s;       // [rows, K/128]
+  const uint8_t* b;       // [N, K] or [E, N, K]
+  const float* b_s;       // [ceil(N/128), K/128] or [E, ...]
+  void* c;                // [rows, N]
+  const int32_t* offsets; // MoE: [E+1] device row offsets
+  int rows;               // M (dense) or R (MoE)
+  int N, K;
+  int E;                  // MoE experts
+  int num_m;              // dense: m tiles; MoE: upper bound on (expert, m-tile) pairs
+  int num_n;              // n tiles
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
+// that each XCD receives a contiguous range of logical tiles, which then
+// share operands in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int q = total / 8, r = total % 8;
+  const int x = id % 8, k = id / 8;
+  return x * q + min(x, r) + k;
+}
+
+// Row `r` of a 128-byte-row LDS tile, lane group g: the 32 bytes of logical
+// chunks 2g and 2g+1 (two 16-byte reads at their swizzled positions).
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
+  const int sw = r & 7;
+  const uint4 lo = *(const uint4*)(tile + r * 128 + (((2 * g) ^ sw) << 4));
+  const uint4 hi = *(const uint4*)(tile + r * 128 + (((2 * g + 1) ^ sw) << 4));
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+template <int BM, int BN, int WM, int WN, int ST, bool OUT_F32, bool MOE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_tile_kernel(GemmParams p) {
+  constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range lies in one weight block");
+  constexpr int MT = WM / 16, NT = WN / 16;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, AS_BYTES = 256 * 4, BS_BYTES = 256 * 4;
+  constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
+  constexpr int A_LOADS = A_BYTES / 4096, B_LOADS = B_BYTES / 4096;   // per thread
+  constexpr int LPS = A_LOADS + B_LOADS + 2;                          // DMA ops per stage
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM <= 256, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int K = p.K, N = p.N;
+  const int nkb = K / 128;
+  const int nbn = (N + 127) / 128;
+
+  // ---- which tile
+  int m_base, m_end, n_base;
+  const uint8_t* B;
+  const float* Bs;
+  {
+    const int total = gridDim.x;
+    const int t = xcd_remap(blockIdx.x, total);
+    if (!MOE) {
+      // Groups of GM m-tiles sweep across n (consecutive tiles share B or A).
+      constexpr int GM = 4;
+      const int group = GM * p.num_n;
+      const int gid = t / group, first_m = gid * GM;
+      const int gsz = min(p.num_m - first_m, GM);
+      const int in = t % group;
+      const int mt = first_m + in % gsz, nt = in / gsz;
+      m_base = mt * BM;
+      m_end = p.rows;
+      n_base = nt * BN;
+      B = p.b;
+      Bs = p.b_s;
+    } else {
+      // t = nt * num_m + gm: consecutive workgroups walk the (expert, m-tile)
+      // list for one n tile, so an expert's m tiles run side by side and share
+      // its weight slab.  The list is rebuilt from the device offsets.
+      const int nt = t / p.num_m, gm = t % p.num_m;
+      int e = -1, mt = 0;
+      {
+        int before = 0;                         // m tiles of experts < chunk start
+        for (int e0 = 0; e0 < p.E && e < 0; e0 += 64) {
+          const int ee = e0 + lane;
+          int cnt = 0;
+          if (ee < p.E) {
+            int lo = p.offsets[ee], hi = p.offsets[ee + 1];
+            lo = min(max(lo, 0), p.rows);
+            hi = min(max(hi, lo), p.rows);
+            cnt = (hi - lo + BM - 1) / BM;
+          }
+          // inclusive prefix sum over the wave
+          int incl = cnt;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+          }
+          const int excl = before + incl - cnt;
+          const bool mine = (ee < p.E) && gm >= excl && gm < excl + cnt;
+          const unsigned long long ball = __ballot(mine);
+          if (ball) {
+            const int src = __ffsll((long long)ball) - 1;
+            e = __shfl(ee, src);
+            mt = gm - __shfl(excl, src);
+          }
+          before += __shfl(incl, 63);
+        }
+      }
+      e = __builtin_amdgcn_readfirstlane(e);
+      mt = __builtin_amdgcn_readfirstlane(mt);
+      if (e < 0) return;                        // past the last real tile (uniform)
+      int lo = p.offsets[e], hi = p.offsets[e + 1];
+      lo = min(max(lo, 0), p.rows);
+      hi = min(max(hi, lo), p.rows);
+      m_base = __builtin_amdgcn_readfirstlane(lo + mt * BM);
+      m_end = __builtin_amdgcn_readfirstlane(hi);
+      n_base = nt * BN;
+      B = p.b + (int64_t)e * N * K;
+      Bs = p.b_s + (int64_t)e * nbn * nkb;
+    }
+  }
+
+  // ---- DMA sources.  Load i of this wave covers the 8 rows 8*(4i+wave) ..
+  // +7 of the tile; lane l takes row l/8 of those and the logical chunk
+  // (l % 8) ^ (row % 8).  Offsets grow by 32 rows per load and 128 bytes per
+  // K block.
+  const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)p.rows * K));
+  const v4i b_rsrc = make_rsrc(B, (uint32_t)((int64_t)N * K));
+  const v4i as_rsrc = make_rsrc(p.a_s, (uint32_t)((int64_t)p.rows * nkb * 4));
+  const v4i bs_rsrc = make_rsrc(Bs, (uint32_t)((int64_t)nbn * nkb * 4));
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  const uint32_t a_voff = (uint32_t)(m_base + 8 * wave + (lane >> 3)) * K + 16 * lchunk;
+  const uint32_t b_voff = (uint32_t)(n_base + 8 * wave + (lane >> 3)) * K + 16 * lchunk;
+  const uint32_t as_voff = (uint32_t)(m_base + (tid % BM)) * nkb * 4;
+  const uint32_t bs_voff = (uint32_t)((n_base + wn * WN) / 128) * nkb * 4;  // this wave's block row
+  const uint32_t row32 = 32u * (uint32_t)K;
+  const uint32_t smem_lds = lds_addr(smem);
+
+  auto issue = [&](int kb, int st) {
+    const uint32_t base = smem_lds + st * STAGE + wave * 1024;
+    const uint32_t koff = (uint32_t)kb * 128;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) dma_b128(a_rsrc, base + i * 4096, a_voff + i * row32 + koff);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      dma_b128(b_rsrc, base + A_BYTES + i * 4096, b_voff + i * row32 + koff);
+    dma_b32(as_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, as_voff + kb * 4);
+    // every lane of the wave fetches the same b_s value of its weight block
+    dma_b32(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + AS_BYTES + wave * 256,
+            bs_voff + kb * 4);
+  };
+
+  v4f acc[NT][MT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int g = lane >> 4, r16 = lane & 15;
+
+  // prologue
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nkb) issue(s, s);
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb % ST;
+    // DMA for kb is complete once at most the later stages' ops are pending.
+    if (kb + ST - 2 < nkb) wait_vmcnt<(ST - 2) * LPS>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (kb + ST - 1 < nkb) issue(kb + ST - 1, (kb + ST - 1) % ST);
+
+    const uint8_t* at = smem + st * STAGE;
+    const uint8_t* bt = at + A_BYTES;
+    const float* ast = (const float*)(at + A_BYTES + B_BYTES);
+    const float bsv = ((const float*)(at + A_BYTES + B_BYTES + AS_BYTES))[wave * 64];
+    v8i bf[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bf[j] = lds_frag(bt, wn * WN + 16 * j + r16, g);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int ml = wm * WM + 16 * t + r16;
+      const v8i af = lds_frag(at, ml, g);
+      const float sc = ast[ml] * bsv;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const v4f pr = mfma_k128(bf[j], af);
+        acc[j][t][0] = __builtin_fmaf(pr[0], sc, acc[j][t][0]);
+        acc[j][t][1] = __builtin_fmaf(pr[1], sc, acc[j][t][1]);
+        acc[j][t][2] = __builtin_fmaf(pr[2], sc, acc[j][t][2]);
+        acc[j][t][3] = __builtin_fmaf(pr[3], sc, acc[j][t][3]);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds C[m][n .. n+3] for each (j, t)
+  const bool vec_ok = (N % 4) == 0;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = m_base + wm * WM + 16 * t + r16;
+    if (m >= m_end) continue;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n_base + wn * WN + 16 * j + 4 * g;
+      if (n >= N) continue;
+      if (OUT_F32) {
+        float* cp = (float*)p.c + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *(float4*)cp = make_float4(acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]);
+        } else {
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) cp[r] = acc[j][t][r];
+        }
+      } else {
+        uint16_t* cp = (uint16_t*)p.c + (int64_t)m * N + n;
+        const uint32_t lo = pack2_bf16(acc[j][t][0], acc[j][t][1]);
+        const uint32_t hi = pack2_bf16(acc[j][t][2], acc[j][t][3]);
+        if (vec_ok && n + 3 < N) {
+          *(uint2*)cp = make_uint2(lo, hi);
+        } else {
+          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
+                                 (uint16_t)(hi >> 16)};
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) cp[r] = h[r];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Skinny kernel (M <= 64): weight streaming for decode-shaped products.
+// ----------------------------------------------------------------------------
+// A workgroup owns 16*NTW rows of B (weights) and all M rows of A.  Its four
+// waves split the K blocks round-robin (wave w takes kb = w, w+4, ...), each
+// streaming its weight fragments straight from HBM into VGPRs (no LDS: no
+// operand is shared between waves), D K blocks in flight per wave.  The four
+// partial accumulators are summed through LDS at the end.
+//
+// Arithmetic.  The FP8 MFMA sums its 128 products in a reduced-precision
+// internal format (measured on gfx950: errors up to ~1.4e-5 of the sum of
+// |products| on normal data and ~2.3e-4 with 50x outliers), while the bf16
+// MFMA on the same values is accurate to ~2e-8.  This kernel is bound by HBM,
+// not by the matrix cores, so it decodes the e4m3 bytes to bf16 in registers
+// (exact: every e4m3 value is a bf16 value) and runs four K = 32 bf16 MFMAs
+// per 128-wide K block; the block's partial is then scaled and added in fp32
+// as in the tile kernel.  K mapping: instruction i, lane group g takes the
+// bytes [32g + 8i, 32g + 8i + 8) of the block for both operands.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Eight e4m3 bytes (two dwords, byte order = element order) -> eight bf16.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  v8bf r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+template <int MT, int NTW, int D, bool OUT_F32>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams p) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int M = p.rows, N = p.N, K = p.K;
+  const int nkb = K / 128;
+  const int n_base = blockIdx.x * (16 * NTW);
+  // Every wave's n rows lie in one weight block only if 16*NTW divides 128.
+  static_assert(128 % (16 * NTW) == 0, "weight block alignment");
+  const int bs_row = n_base / 128;
+
+  // byte offsets of this lane's operand rows (clamped inside the matrices)
+  int64_t b_row_off[NTW], a_row_off[MT];
+  int a_s_row[MT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) b_row_off[j] = (int64_t)min(n_base + 16 * j + r16, N - 1) * K + 32 * g;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = min(16 * t + r16, M - 1);
+    a_row_off[t] = (int64_t)m * K + 32 * g;
+    a_s_row[t] = m * nkb;
+  }
+
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  struct Slot {
+    v4u b[NTW][2];
+    v4u a[MT][2];
+    float as[MT];
+  };
+  auto load = [&](Slot& s, int kb) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      // weights are read exactly once: non-temporal loads keep them out of L2
+      const v4u* src = (const v4u*)(p.b + b_row_off[j] + (int64_t)kb * 128);
+      s.b[j][0] = __builtin_nontemporal_load(src);
+      s.b[j][1] = __builtin_nontemporal_load(src + 1);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const v4u* src = (const v4u*)(p.a + a_row_off[t] + (int64_t)kb * 128);
+      s.a[t][0] = src[0];
+      s.a[t][1] = src[1];
+      s.as[t] = p.a_s[a_s_row[t] + kb];
+    }
+  };
+
+  v4f acc[NTW][MT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const Slot& s, int kb) {
+    const float bsv = p.b_s[(int64_t)bs_row * nkb + kb];
+    v8bf af[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[t][i] = e4m3x8_to_bf16(s.a[t][i / 2][2 * (i % 2)], s.a[t][i / 2][2 * (i % 2) + 1]);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      v8bf bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bf[i] = e4m3x8_to_bf16(s.b[j][i / 2][2 * (i % 2)], s.b[j][i / 2][2 * (i % 2) + 1]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        v4f pr = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], af[t][i], pr, 0, 0, 0);
+        const float sc = s.as[t] * bsv;
+        acc[j][t][0] = __builtin_fmaf(pr[0], sc, acc[j][t][0]);
+        acc[j][t][1] = __builtin_fmaf(pr[1], sc, acc[j][t][1]);
+        acc[j][t][2] = __builtin_fmaf(pr[2], sc, acc[j][t][2]);
+        acc[j][t][3] = __builtin_fmaf(pr[3], sc, acc[j][t][3]);
+      }
+    }
+  };
+
+  // this wave's K blocks: kb = wave + 4 i, i < cnt
+  const int cnt = nkb > wave ? (nkb - wave + 3) / 4 : 0;
+  Slot ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (d < cnt) load(ring[d], wave + 4 * d);
+  for (int i0 = 0; i0 < cnt; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      if (i < cnt) {
+        if (i + D - 1 < cnt) load(ring[(d + D - 1) % D], wave + 4 * (i + D - 1));
+        compute(ring[d], wave + 4 * i);
+      }
+    }
+  }
+
+  // ---- cross-wave reduction through LDS, then store
+  constexpr int NV = NTW * MT * 4;                 // values per lane
+  __shared__ float red[4][NV][64];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(j * MT + t) * 4 + r][lane] = acc[j][t][r];
+  __syncthreads();
+  for (int idx = tid; idx < NV * 64; idx += 256) {
+    const int v = idx / 64, l = idx % 64;
+    const float sum = red[0][v][l] + red[1][v][l] + red[2][v][l] + red[3][v][l];
+    const int r = v % 4, jt = v / 4, t = jt % MT, j = jt / MT;
+    const int m = 16 * t + (l & 15);
+    const int n = n_base + 16 * j + 4 * (l >> 4) + r;
+    if (m < M && n < N) {
+      if (OUT_F32) ((float*)p.c)[(int64_t)m * N + n] = sum;
+      else ((uint16_t*)p.c)[(int64_t)m * N + n] = (uint16_t)(pack2_bf16(sum, 0.0f) & 0xFFFFu);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Launchers
+// ----------------------------------------------------------------------------
+namespace {
+
+template <int BM, int BN, int WM, int WN, int ST, bool MOE>
+hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
+  if (out_f32)
+    gemm_tile_kernel<BM, BN, WM, WN, ST, true, MOE><<<dim3(grid), dim3(256), 0, stream>>>(p);
+  else
+    gemm_tile_kernel<BM, BN, WM, WN, ST, false, MOE><<<dim3(grid), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t run_skinny(const GemmParams& p, bool out_f32, hipStream_t stream) {
+  constexpr int NTW = 4, D = 3;
+  const int grid = (p.N + 16 * NTW - 1) / (16 * NTW);
+  if (out_f32)
+    gemm_skinny_kernel<MT, NTW, D, true><<<dim3(grid), dim3(256), 0, stream>>>(p);
+  else
+    gemm_skinny_kernel<MT, NTW, D, false><<<dim3(grid), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+                       int64_t M, int64_t N, int64_t K, bool out_f32, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmParams p{};
+  p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
+  p.offsets = nullptr; p.rows = (int)M; p.N = (int)N; p.K = (int)K; p.E = 0;
+  if (M <= 16) return run_skinny<1>(p, out_f32, stream);
+  if (M <= 32) return run_skinny<2>(p, out_f32, stream);
+  if (M <= 64) return run_skinny<4>(p, out_f32, stream);
+  constexpr int BM = 256, BN = 128;
+  p.num_m = (int)((M + BM - 1) / BM);
+  p.num_n = (int)((N + BN - 1) / BN);
+  return run_tile<BM, BN, 128, 64, 3, false>(p, out_f32, p.num_m * p.num_n, stream);
+}
+
+hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
+                           const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N,
+                           int64_t K, bool out_f32, hipStream_t stream) {
+  if (R == 0 || E == 0 || N == 0) return hipSuccess;
+  GemmParams p{};
+  p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
+  p.offsets = offsets; p.rows = (int)R; p.N = (int)N; p.K = (int)K; p.E = (int)E;
+  constexpr int BM = 64, BN = 256;
+  // sum_e ceil(rows_e / BM) <= R / BM + E
+  p.num_m = (int)(R / BM + E);
+  p.num_n = (int)((N + BN - 1) / BN);
+  return run_tile<BM, BN, 64, 64, 3, true>(p, out_f32, p.num_m * p.num_n, stream);
+}
+
+}  // namespace fp8bs

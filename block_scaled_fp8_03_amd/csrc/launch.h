@@ -1,0 +1,23 @@
+// launch.h -- internal kernel launchers (host side).  Arguments have been
+// validated by the C ABI layer before these are called; each returns the
+// hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
+                            hipStream_t stream);
+hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K,
+                               hipStream_t stream);
+hipError_t launch_weight_dequant(const void* w, const float* s, void* y, int64_t N, int64_t K,
+                                 hipStream_t stream);
+hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+                       int64_t M, int64_t N, int64_t K, bool out_f32, hipStream_t stream);
+hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
+                           const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N,
+                           int64_t K, bool out_f32, hipStream_t stream);
+
+}  // namespace fp8bs

@@ -1,0 +1,248 @@
+// quant.hip -- block quantisation kernels for gfx950:
+//   act_quant      1 x 128 activation blocks -> e4m3 + float32 scale
+//                  ("DeepSeek-V3 Administrator & Developer Guide" 8.5.1;
+//                  ue8m0 per the "DeepSeek-V3 User Guide" FAQ)
+//   weight_quant   128 x 128 weight blocks, same rule (scale layout of
+//                  Admin guide 6.3)
+//   weight_dequant e4m3 x block scale -> bf16 (Admin guide 8.5.2)
+// All three are HBM-streaming kernels: every lane moves 16-byte vectors,
+// a 16-lane DPP row owns one 128-element activation block, and the per-block
+// reductions stay inside registers.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8bs {
+
+// ----------------------------------------------------------------------------
+// act_quant
+// ----------------------------------------------------------------------------
+// The input is a flat sequence of 128-element blocks (K % 128 == 0, row-major),
+// and block b's scale lives at s[b] ([M, K/128] row-major is that order).
+// A 16-lane row handles one block: lane i holds elements 8i .. 8i+7 (16 bytes
+// of bf16) and writes their 8 e4m3 bytes.  A 256-thread workgroup covers 16
+// blocks per pass and kAqPasses passes, all loads issued before any use.
+constexpr int kAqThreads = 256;
+constexpr int kAqPasses = 4;
+constexpr int kAqBlocksPerWg = (kAqThreads / 16) * kAqPasses;
+
+template <bool UE8M0>
+__global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __restrict__ x,
+                                                               uint2* __restrict__ q,
+                                                               float* __restrict__ s,
+                                                               int64_t nblocks) {
+  const int lane16 = threadIdx.x & 15;
+  const int row = threadIdx.x >> 4;
+  const int64_t first = (int64_t)blockIdx.x * kAqBlocksPerWg + row;
+  uint4 v[kAqPasses];
+#pragma unroll
+  for (int u = 0; u < kAqPasses; ++u) {
+    const int64_t b = first + u * (kAqThreads / 16);
+    v[u] = (b < nblocks) ? x[b * 16 + lane16] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kAqPasses; ++u) {
+    const int64_t b = first + u * (kAqThreads / 16);
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, f32_bits(f[i]) & 0x7FFFFFFFu);
+    m = row16_max_u32(m);                      // amax of the whole 128-block
+    const float sc = block_scale<UE8M0>(bits_f32(m));
+    const float r = __fdiv_rn(1.0f, sc);
+    uint2 o;
+    o.x = pack4_e4m3(div_markstein(f[0], sc, r), div_markstein(f[1], sc, r),
+                     div_markstein(f[2], sc, r), div_markstein(f[3], sc, r));
+    o.y = pack4_e4m3(div_markstein(f[4], sc, r), div_markstein(f[5], sc, r),
+                     div_markstein(f[6], sc, r), div_markstein(f[7], sc, r));
+    if (b < nblocks) {
+      q[b * 16 + lane16] = o;
+      if (lane16 == 0) s[b] = sc;
+    }
+  }
+}
+
+hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
+                            hipStream_t stream) {
+  const int64_t nblocks = M * (K / kBlock);
+  if (nblocks == 0) return hipSuccess;
+  const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
+  if (ue8m0)
+    act_quant_kernel<true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
+        (const uint4*)x, (uint2*)q, s, nblocks);
+  else
+    act_quant_kernel<false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
+        (const uint4*)x, (uint2*)q, s, nblocks);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// weight_quant: one 256-thread workgroup per 128 x 128 block.  Thread t owns
+// row t/2 and the 64 columns (t%2)*64 .. +63 of the block.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float block_amax_256(uint32_t m, uint32_t* red) {
+  m = wave_max_u32(m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  return bits_f32(m);
+}
+
+__global__ __launch_bounds__(256) void weight_quant_kernel(const uint16_t* __restrict__ w,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ s, int64_t N,
+                                                           int64_t K) {
+  __shared__ uint32_t red[4];
+  const int64_t bk = blockIdx.x, bn = blockIdx.y;
+  const int64_t nbk = (K + kBlock - 1) / kBlock;
+  const int64_t n = bn * kBlock + (threadIdx.x >> 1);
+  const int64_t k0 = bk * kBlock + (threadIdx.x & 1) * 64;
+  const bool full = (bn + 1) * kBlock <= N && (bk + 1) * kBlock <= K && (K % 16) == 0;
+  if (full) {
+    // Interior block with 16-byte aligned rows: vector path.
+    const uint4* src = (const uint4*)(w + n * K + k0);
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[i];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ws[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        m = max(m, max(f32_bits(bf16_lo(ws[j])) & 0x7FFFFFFFu, f32_bits(bf16_hi(ws[j])) & 0x7FFFFFFFu));
+    }
+    const float sc = block_scale<false>(block_amax_256(m, red));
+    const float r = __fdiv_rn(1.0f, sc);
+    uint4* dst = (uint4*)(q + n * K + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a[4] = {v[2 * i].x, v[2 * i].y, v[2 * i].z, v[2 * i].w};
+      const uint32_t b[4] = {v[2 * i + 1].x, v[2 * i + 1].y, v[2 * i + 1].z, v[2 * i + 1].w};
+      uint4 o;
+      o.x = pack4_e4m3(div_markstein(bf16_lo(a[0]), sc, r), div_markstein(bf16_hi(a[0]), sc, r),
+                       div_markstein(bf16_lo(a[1]), sc, r), div_markstein(bf16_hi(a[1]), sc, r));
+      o.y = pack4_e4m3(div_markstein(bf16_lo(a[2]), sc, r), div_markstein(bf16_hi(a[2]), sc, r),
+                       div_markstein(bf16_lo(a[3]), sc, r), div_markstein(bf16_hi(a[3]), sc, r));
+      o.z = pack4_e4m3(div_markstein(bf16_lo(b[0]), sc, r), div_markstein(bf16_hi(b[0]), sc, r),
+                       div_markstein(bf16_lo(b[1]), sc, r), div_markstein(bf16_hi(b[1]), sc, r));
+      o.w = pack4_e4m3(div_markstein(bf16_lo(b[2]), sc, r), div_markstein(bf16_hi(b[2]), sc, r),
+                       div_markstein(bf16_lo(b[3]), sc, r), div_markstein(bf16_hi(b[3]), sc, r));
+      dst[i] = o;
+    }
+    if (threadIdx.x == 0) s[bn * nbk + bk] = sc;
+  } else {
+    // Edge block or unaligned rows: element by element, masked.
+    uint32_t m = 0;
+    if (n < N)
+      for (int j = 0; j < 64; ++j)
+        if (k0 + j < K) m = max(m, f32_bits(bf16_lo(w[n * K + k0 + j])) & 0x7FFFFFFFu);
+    const float sc = block_scale<false>(block_amax_256(m, red));
+    const float r = __fdiv_rn(1.0f, sc);
+    if (n < N)
+      for (int j = 0; j < 64; j += 4) {
+        float f[4];
+        for (int t = 0; t < 4; ++t)
+          f[t] = (k0 + j + t < K) ? div_markstein(bf16_lo(w[n * K + k0 + j + t]), sc, r) : 0.0f;
+        const uint32_t o = pack4_e4m3(f[0], f[1], f[2], f[3]);
+        for (int t = 0; t < 4; ++t)
+          if (k0 + j + t < K) q[n * K + k0 + j + t] = (uint8_t)(o >> (8 * t));
+      }
+    if (threadIdx.x == 0) s[bn * nbk + bk] = sc;
+  }
+}
+
+hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K,
+                               hipStream_t stream) {
+  if (N == 0 || K == 0) return hipSuccess;
+  const int64_t nbn = (N + kBlock - 1) / kBlock, nbk = (K + kBlock - 1) / kBlock;
+  weight_quant_kernel<<<dim3((unsigned)nbk, (unsigned)nbn), dim3(256), 0, stream>>>(
+      (const uint16_t*)w, (uint8_t*)q, s, N, K);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// weight_dequant
+// ----------------------------------------------------------------------------
+// Vector path (K % 16 == 0): lane l of wave w handles the 16-column chunk
+// blockIdx.x*64 + l of rows blockIdx.y*kDqRows + w + 4i; a chunk never
+// straddles a 128-column scale block.  Per row: one 16-byte load, 16
+// conversions, 16 multiplies, 8 bf16 pair packs, one 32-byte store.
+constexpr int kDqRows = 16;
+
+__global__ __launch_bounds__(256) void weight_dequant_kernel(const uint4* __restrict__ w,
+                                                             const float* __restrict__ s,
+                                                             uint4* __restrict__ y, int64_t N,
+                                                             int64_t K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t kc = (int64_t)blockIdx.x * 64 + lane;      // 16-element chunk in the row
+  const int64_t kchunks = K / 16;
+  if (kc >= kchunks) return;
+  const int64_t nbk = (K + kBlock - 1) / kBlock;
+  const int64_t sb = (kc * 16) / kBlock;
+  constexpr int kPer = kDqRows / 4;
+  uint4 v[kPer];
+  float sc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t n = (int64_t)blockIdx.y * kDqRows + wave + 4 * i;
+    if (n < N) {
+      v[i] = w[n * kchunks + kc];
+      sc[i] = s[(n / kBlock) * nbk + sb];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t n = (int64_t)blockIdx.y * kDqRows + wave + 4 * i;
+    if (n >= N) continue;
+    const uint32_t ws[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);   // bytes 0, 1
+      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);    // bytes 2, 3
+      o[2 * j] = pack2_bf16(__fmul_rn(lo.x, sc[i]), __fmul_rn(lo.y, sc[i]));
+      o[2 * j + 1] = pack2_bf16(__fmul_rn(hi.x, sc[i]), __fmul_rn(hi.y, sc[i]));
+    }
+    uint4* dst = y + (n * kchunks + kc) * 2;
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Generic path (any K): one element per thread.
+__global__ __launch_bounds__(256) void weight_dequant_scalar_kernel(const uint8_t* __restrict__ w,
+                                                                    const float* __restrict__ s,
+                                                                    uint16_t* __restrict__ y,
+                                                                    int64_t N, int64_t K) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N * K) return;
+  const int64_t n = i / K, k = i % K;
+  const int64_t nbk = (K + kBlock - 1) / kBlock;
+  const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+  const float p = __fmul_rn(f.x, s[(n / kBlock) * nbk + k / kBlock]);
+  y[i] = (uint16_t)(pack2_bf16(p, 0.0f) & 0xFFFFu);
+}
+
+hipError_t launch_weight_dequant(const void* w, const float* s, void* y, int64_t N, int64_t K,
+                                 hipStream_t stream) {
+  if (N == 0 || K == 0) return hipSuccess;
+  if (K % 16 == 0) {
+    const int64_t gx = (K / 16 + 63) / 64, gy = (N + kDqRows - 1) / kDqRows;
+    weight_dequant_kernel<<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream>>>(
+        (const uint4*)w, s, (uint4*)y, N, K);
+  } else {
+    const int64_t grid = (N * K + 255) / 256;
+    weight_dequant_scalar_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+        (const uint8_t*)w, s, (uint16_t*)y, N, K);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,159 @@
+/*
+ * fp8bs.h -- C ABI of the block-scaled FP8 linear library for AMD MI355X
+ * (gfx950).  Every entry point takes plain device pointers, sizes and a HIP
+ * stream, enqueues its kernels on that stream and returns without waiting.
+ *
+ * Conventions shared by all entry points
+ *   - Tensors are dense, row-major and contiguous; sizes are element counts.
+ *   - "e4m3" is the OCP float8 E4M3 "fn" byte format (torch.float8_e4m3fn):
+ *     bias 7, no infinities, 0x7F/0xFF are NaN, largest magnitude 448.
+ *   - "bf16" tensors are passed as their 16-bit patterns (torch.bfloat16).
+ *   - Block size is 128 everywhere: activations carry one float32 scale per
+ *     1 x 128 block along K, weights one per 128 x 128 block.  A scale is the
+ *     dequantisation multiplier: real value = decode(code) * scale.
+ *   - The caller owns all memory.  The library never allocates or frees,
+ *     keeps no global state, and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream) on the
+ *     current HIP device; all pointers must be device (or managed) memory of
+ *     that device.
+ *   - Arguments are validated on the host before any HIP call.  A non-zero
+ *     status means nothing was enqueued (except FP8BS_ERR_HIP, returned when
+ *     a kernel launch itself fails).  Faults inside kernels are reported
+ *     asynchronously by HIP, as for any kernel.
+ *   - Inputs holding NaN are outside the contract (NaN propagates; payloads
+ *     are not specified).
+ *
+ * The operations follow the DeepSeek-V3 inference pages: "DeepSeek-V3
+ * Administrator & Developer Guide" sections 8.5.1 (act_quant_kernel), 8.5.2
+ * (weight_dequant_kernel), 8.5.3 (fp8_gemm_kernel), 6.3 (the FP8 path and
+ * the weight scale shape), 6.4 (MoE expert loop); "DeepSeek-V3 User Guide"
+ * section 7 FAQ (scale_fmt ue8m0) and section 6 (K must be a multiple of 128).
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FP8BS_OK          0
+#define FP8BS_ERR_NULL    1  /* a required pointer is NULL */
+#define FP8BS_ERR_SHAPE   2  /* negative size, K not a multiple of 128, size limit */
+#define FP8BS_ERR_ALIGN   3  /* a pointer is not 16-byte aligned */
+#define FP8BS_ERR_ENUM    4  /* unknown scale_fmt / out_dtype */
+#define FP8BS_ERR_HIP     5  /* a HIP launch failed */
+#define FP8BS_ERR_ALIAS   6  /* an output overlaps an input */
+
+/* Scale formats for activation quantisation. */
+#define FP8BS_SCALE_FP32  0  /* s = max(amax, 1e-4) / 448 as float32 */
+#define FP8BS_SCALE_UE8M0 1  /* s rounded up to the next power of two */
+
+/* Output element types of the GEMMs. */
+#define FP8BS_OUT_BF16    0
+#define FP8BS_OUT_F32     1
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8bs_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fp8bs_version(void);
+
+/*
+ * act_quant -- per-1x128-block activation quantisation.
+ * Admin guide 8.5.1; ue8m0 per the User guide FAQ.
+ *
+ * For every row m and block j (columns 128j .. 128j+127):
+ *   amax = max |x|,  s = RN32(max(amax, 1e-4f) / 448)   (IEEE division),
+ *   ue8m0: s = smallest power of two >= s,
+ *   q = e4m3(RN32(x / s))  (correctly rounded division, then round to nearest
+ *   even onto the e4m3 grid, saturating at +-448).
+ *
+ *   x_bf16  in   bf16 [M, K]
+ *   q_e4m3  out  e4m3 [M, K]          (must not overlap x)
+ *   s       out  float32 [M, K/128]
+ *   M >= 0 (0 = no-op), K >= 0 with K % 128 == 0 (else FP8BS_ERR_SHAPE).
+ *   All three pointers 16-byte aligned except `s` (4-byte).
+ */
+int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64_t K,
+                    int scale_fmt, void* stream);
+
+/*
+ * weight_quant -- 128x128-block weight quantisation with the same rule as
+ * act_quant (fp32 scale format).  The pages ship weights already quantised
+ * (Admin guide 6.3: one float32 scale per 128 x 128 block, shape
+ * ceil(N/128) x ceil(K/128)); this entry point produces that form from a
+ * bf16 weight.  A partial edge block uses the amax of its own elements.
+ *
+ *   w_bf16  in   bf16 [N, K]
+ *   q_e4m3  out  e4m3 [N, K]
+ *   s       out  float32 [ceil(N/128), ceil(K/128)]
+ *   N, K >= 0, any values.
+ */
+int fp8bs_weight_quant(const void* w_bf16, void* q_e4m3, float* s, int64_t N, int64_t K,
+                       void* stream);
+
+/*
+ * weight_dequant -- Admin guide 8.5.2:
+ *   y[n, k] = bf16_RNE( RN32( decode(w[n, k]) * s[n/128, k/128] ) ).
+ *
+ *   w_e4m3  in   e4m3 [N, K]
+ *   s       in   float32 [ceil(N/128), ceil(K/128)]
+ *   y_bf16  out  bf16 [N, K]
+ *   N, K >= 0, any values (ragged edge blocks allowed).
+ */
+int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64_t N, int64_t K,
+                         void* stream);
+
+/*
+ * gemm -- block-scaled FP8 GEMM, Admin guide 8.5.3 (nn.Linear layout):
+ *   C[m, n] = sum_kb ( sum_{k in block kb} a[m, k] * b[n, k] )
+ *                    * a_s[m, kb] * b_s[n / 128, kb]
+ * with float32 accumulation; each 128-wide K block's partial product is
+ * scaled once and added to the accumulator.
+ *
+ *   a    in   e4m3 [M, K]              (activations, from fp8bs_act_quant)
+ *   a_s  in   float32 [M, K/128]
+ *   b    in   e4m3 [N, K]              (weight, out x in)
+ *   b_s  in   float32 [ceil(N/128), K/128]
+ *   c    out  [M, N], bf16 (RNE) or float32 per out_dtype
+ *   M >= 0 (0 = no-op), N >= 0, K >= 128 with K % 128 == 0;
+ *   (M + 256) * K < 2^32 and (N + 256) * K < 2^32 (32-bit operand offsets).
+ *   a, b, c 16-byte aligned; a_s, b_s 4-byte aligned.
+ */
+int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+               int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
+
+/*
+ * moe_gemm -- grouped block-scaled FP8 GEMM over E experts in one launch,
+ * the per-expert products of the MoE loop (Admin guide 6.4), each computed as
+ * in fp8bs_gemm.  Rows [offsets[e], offsets[e+1]) of `a` (grouped by expert)
+ * are multiplied by expert e's weight:
+ *   C[r, n] = sum_kb (sum_k a[r, k] * b[e, n, k]) * a_s[r, kb] * b_s[e, n/128, kb].
+ *
+ *   a        in   e4m3 [R, K]
+ *   a_s      in   float32 [R, K/128]
+ *   b        in   e4m3 [E, N, K]
+ *   b_s      in   float32 [E, ceil(N/128), K/128]
+ *   offsets  in   DEVICE int32 [E+1]: offsets[0] = 0, non-decreasing,
+ *                 offsets[E] = R (precondition, not checked on the host so
+ *                 that no device->host copy is needed; the kernel clamps
+ *                 every range to [0, R] so a violation cannot write outside c)
+ *   c        out  [R, N] bf16 or float32; rows not covered by any expert are
+ *                 left untouched
+ *   R, E >= 0 (either 0 = no-op), N >= 0, K >= 128 with K % 128 == 0;
+ *   (R + 256) * K < 2^32 and (N + 256) * K < 2^32.
+ * The launch grid is sized on the host from R and E alone; experts with no
+ * rows cost (almost) nothing.
+ */
+int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
+                   const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N, int64_t K,
+                   int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every function include/fp8bs.h declares, and rejects bad arguments on the host
+before any HIP call (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_03_amd as fp8bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+OK, NULL, SHAPE, ALIGN, ENUM, HIP, ALIAS = 0, 1, 2, 3, 4, 5, 6
+P0 = 0x100000        # fake, 16-byte aligned "device" addresses: only compared, never touched
+P1 = 0x10000000
+P2 = 0x20000000
+P3 = 0x30000000
+P4 = 0x40000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fp8bs.library_path):
+        from block_scaled_fp8_03_amd import build
+        build.build()
+    return fp8bs.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8bs_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fp8bs_act_quant", "fp8bs_weight_dequant", "fp8bs_gemm", "fp8bs_moe_gemm",
+              "fp8bs_weight_quant", "fp8bs_status_string", "fp8bs_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(0, 8):
+        s = L.fp8bs_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert L.fp8bs_status_string(0) == b"ok"
+    assert L.fp8bs_version() >= 10000
+
+
+def test_act_quant_validation(L):
+    f = L.fp8bs_act_quant
+    assert f(P0, P1, P2, 4, 100, 0, None) == SHAPE            # K % 128
+    assert f(P0, P1, P2, -1, 128, 0, None) == SHAPE
+    assert f(P0, P1, P2, 4, 128, 7, None) == ENUM
+    assert f(None, P1, P2, 4, 128, 0, None) == NULL
+    assert f(P0, None, P2, 4, 128, 0, None) == NULL
+    assert f(P0 + 8, P1, P2, 4, 128, 0, None) == ALIGN
+    assert f(P0, P1 + 4, P2, 4, 128, 0, None) == ALIGN
+    assert f(P0, P1, P2 + 2, 4, 128, 0, None) == ALIGN
+    assert f(P0, P0 + 256, P2, 4, 128, 0, None) == ALIAS    # q inside x
+    assert f(P0, P1, P1 + 64, 4, 128, 0, None) == ALIAS     # s inside q
+    assert f(None, None, None, 0, 128, 0, None) == OK       # empty: no launch
+    assert f(None, None, None, 5, 0, 1, None) == OK
+
+
+def test_weight_quant_and_dequant_validation(L):
+    assert L.fp8bs_weight_quant(P0, P1, P2, -3, 5, None) == SHAPE
+    assert L.fp8bs_weight_quant(None, P1, P2, 3, 5, None) == NULL
+    assert L.fp8bs_weight_quant(P0 + 2, P1, P2, 3, 5, None) == ALIGN
+    assert L.fp8bs_weight_quant(P0, P0, P2, 3, 5, None) == ALIAS
+    assert L.fp8bs_weight_quant(None, None, None, 0, 5, None) == OK
+    assert L.fp8bs_weight_dequant(P0, P1, P2, 3, -5, None) == SHAPE
+    assert L.fp8bs_weight_dequant(P0, None, P2, 3, 5, None) == NULL
+    assert L.fp8bs_weight_dequant(P0, P1, P2 + 8, 3, 5, None) == ALIGN
+    assert L.fp8bs_weight_dequant(P0, P1, P0, 3, 5, None) == ALIAS
+    assert L.fp8bs_weight_dequant(None, None, None, 7, 0, None) == OK
+
+
+def test_gemm_validation(L):
+    g = L.fp8bs_gemm
+    assert g(P0, P1, P2, P3, P4, 4, 4, 100, 0, None) == SHAPE        # K % 128
+    assert g(P0, P1, P2, P3, P4, 4, 4, 0, 0, None) == SHAPE          # K = 0
+    assert g(P0, P1, P2, P3, P4, -4, 4, 128, 0, None) == SHAPE
+    assert g(P0, P1, P2, P3, P4, 4, 4, 128, 2, None) == ENUM
+    assert g(P0, P1, None, P3, P4, 4, 4, 128, 0, None) == NULL
+    assert g(P0, P1, P2, P3, P4 + 4, 4, 4, 128, 1, None) == ALIGN
+    assert g(P0, P1, P2, P3 + 1, P4, 4, 4, 128, 1, None) == ALIGN
+    assert g(P0, P1, P2, P3, P0, 4, 4, 128, 1, None) == ALIAS         # C over A
+    assert g(P0, P1, P2, P3, P3 - 16, 4, 4, 128, 1, None) == ALIAS    # C runs into b_s
+    assert g(None, None, None, None, None, 0, 4, 128, 0, None) == OK  # M = 0
+    assert g(None, None, None, None, None, 4, 0, 128, 0, None) == OK  # N = 0
+    big = 1 << 25
+    assert g(P0, P1, P2, P3, P4, big, 4, 128, 0, None) == SHAPE       # M*K >= 2^32
+
+
+def test_moe_gemm_validation(L):
+    m = L.fp8bs_moe_gemm
+    assert m(P0, P1, P2, P3, P4, P4 + 4096, 8, 2, 4, 100, 0, None) == SHAPE
+    assert m(P0, P1, P2, P3, P4, P4 + 4096, 8, -2, 4, 128, 0, None) == SHAPE
+    assert m(P0, P1, P2, P3, P4, P4 + 4096, 8, 2, 4, 128, 9, None) == ENUM
+    assert m(P0, P1, P2, P3, None, P4 + 4096, 8, 2, 4, 128, 0, None) == NULL
+    assert m(P0, P1, P2, P3, P4 + 2, P4 + 4096, 8, 2, 4, 128, 0, None) == ALIGN
+    assert m(P0, P1, P2, P3, P4, P0, 8, 2, 4, 128, 0, None) == ALIAS
+    assert m(None, None, None, None, None, None, 0, 2, 4, 128, 0, None) == OK
+    assert m(None, None, None, None, None, None, 8, 0, 4, 128, 0, None) == OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        fp8bs.act_quant(x)

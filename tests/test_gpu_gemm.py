@@ -1,0 +1,246 @@
+"""GPU parity of the block-scaled FP8 GEMM and the grouped MoE GEMM against the
+CPU oracle (binary64), through the C ABI.  Bar, element-wise:
+|gpu - ref| <= 1e-2 |ref| + 1e-3, on the float32 output and on the bf16 output.
+Small shapes are compared in full (several tiles, ragged M and N tails); the
+full-size workloads are compared in full where the oracle is quick (decode)
+and on sampled points elsewhere (whole rows, whole columns, tile corners and
+random points), in the launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_03_amd as fp8bs
+import oracle
+from block_scaled_fp8_03_amd import inputs
+from gpu_util import DEV, assert_close, to_dev_f32, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+
+
+def rand_operands(M, N, K, seed, a_std=1.0, w_std=0.02, outliers=False):
+    """Quantised operands made by the oracle from seeded bf16 draws."""
+    x = inputs.normal_bf16((M, K), a_std, seed, outlier_frac=0.01 if outliers else 0.0,
+                           outlier_mult=50.0)
+    w = inputs.normal_bf16((N, K), w_std, seed + 1)
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), oracle.FMT_FP32)
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w))
+    return a, a_s, b, b_s
+
+
+def run_gemm(a, a_s, b, b_s, out_dtype):
+    c = fp8bs.fp8_gemm(to_dev_u8(a), to_dev_f32(a_s), to_dev_u8(b), to_dev_f32(b_s), out_dtype)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy()
+
+
+SMALL = [(16, 256, 256), (1, 1, 128), (5, 7, 128), (33, 130, 256), (64, 64, 128),
+         (65, 200, 384), (257, 129, 256), (300, 520, 1024), (512, 384, 640), (2, 300, 7168)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_gemm_small(M, N, K):
+    a, a_s, b, b_s = rand_operands(M, N, K, 3000 + M * 7 + N)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    assert_close(run_gemm(a, a_s, b, b_s, torch.float32), ref, f"gemm[{M}x{N}x{K}] f32")
+    assert_close(run_gemm(a, a_s, b, b_s, torch.bfloat16), ref, f"gemm[{M}x{N}x{K}] bf16")
+
+
+def extreme_operands(M, N, K, seed):
+    """Codes spanning the whole e4m3 range and scales from 2^-30 to 2^10."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    b = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x7E
+    b[(b & 0x7F) == 0x7F] = 0xFE
+    a_s = (2.0 ** rng.uniform(-30, 10, (M, K // 128))).astype(np.float32)
+    b_s = (2.0 ** rng.uniform(-10, 5, (-(-N // 128), K // 128))).astype(np.float32)
+    return a, a_s, b, b_s
+
+
+def test_gemm_extreme_scales_skinny():
+    """M <= 64 takes the bf16-MFMA path, whose block sums are fp32-accurate: the
+    plain bar holds even for full-range random codes."""
+    a, a_s, b, b_s = extreme_operands(48, 150, 512, 7)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    assert_close(run_gemm(a, a_s, b, b_s, torch.float32), ref, "gemm extreme scales (M=48)")
+
+
+def test_gemm_extreme_scales_tile():
+    """The FP8-MFMA tile path on full-range random codes.  The FP8 MFMA adds its
+    128 products in a reduced-precision internal format (measured worst case
+    ~2^-12 of the sum of |products|), so this stress case, unlike the
+    workloads, gets an explicit hardware term: 2^-11 * sum_kb |a_s b_s| sum_k
+    |a b|, i.e. the oracle GEMM of the magnitudes."""
+    a, a_s, b, b_s = extreme_operands(70, 150, 512, 8)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    mag = oracle.gemm(a & 0x7F, a_s, b & 0x7F, b_s)
+    got = run_gemm(a, a_s, b, b_s, torch.float32).astype(np.float64)
+    err = np.abs(got - ref)
+    bound = 1e-2 * np.abs(ref) + 1e-3 + 2.0 ** -11 * mag
+    assert np.all(err <= bound), (err / bound).max()
+
+
+def test_tiny_linear_end_to_end():
+    """The tiny FP8 linear: x bf16 [16, 256] ~ N(0,1), W [256, 256] ~ N(0, 0.02)
+    quantised to 2x2 blocks; act_quant on the GPU then the GEMM."""
+    x = inputs.normal_bf16((16, 256), 1.0, inputs.seed_for(1, 0))
+    w = inputs.normal_bf16((256, 256), 0.02, inputs.seed_for(1, 1))
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w))
+    y = fp8bs.linear(x.to(DEV), to_dev_u8(b), to_dev_f32(b_s), "fp32", torch.float32)
+    torch.cuda.synchronize()
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), oracle.FMT_FP32)
+    assert_close(y.cpu().numpy(), oracle.gemm(a, a_s, b, b_s), "tiny linear")
+
+
+def sample_points(M, N, rng, n_random=4000):
+    rows, cols = [], []
+    for m in sorted({0, M - 1, M // 2, min(255, M - 1), min(256, M - 1)}):     # whole rows
+        rows += [m] * N
+        cols += list(range(N))
+    for n in sorted({0, N - 1, N // 3, min(127, N - 1), min(128, N - 1)}):      # whole columns
+        rows += list(range(M))
+        cols += [n] * M
+    rows += list(rng.integers(0, M, n_random))
+    cols += list(rng.integers(0, N, n_random))
+    return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
+def full_size_case(cfg, M, N, K, seed_x, seed_w, fmt=oracle.FMT_FP32, outliers=False, full=False):
+    x = inputs.normal_bf16((M, K), 1.0, seed_x, outlier_frac=0.01 if outliers else 0.0,
+                           outlier_mult=50.0)
+    w = inputs.normal_bf16((N, K), 0.02, seed_w)
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w))
+    del w
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), fmt)
+    # act_quant on the GPU as in the benchmark's linear, then the GEMM
+    qd, sd = fp8bs.act_quant(x.to(DEV), fmt)
+    bd, bsd = to_dev_u8(b), to_dev_f32(b_s)
+    c32 = fp8bs.fp8_gemm(qd, sd, bd, bsd, torch.float32)
+    c16 = fp8bs.fp8_gemm(qd, sd, bd, bsd, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(qd.view(torch.uint8).cpu().numpy(), a)
+    if full:
+        ref = oracle.gemm(a, a_s, b, b_s)
+        assert_close(c32.cpu().numpy(), ref, f"gemm[{M}x{N}x{K}] f32")
+        assert_close(c16.float().cpu().numpy(), ref, f"gemm[{M}x{N}x{K}] bf16")
+        return
+    rows, cols = sample_points(M, N, np.random.default_rng(seed_x))
+    ref = oracle.gemm_points(a, a_s, b, b_s, rows, cols)
+    rt, ct = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+    assert_close(c32[rt, ct].cpu().numpy(), ref, f"gemm[{M}x{N}x{K}] f32 sampled")
+    assert_close(c16[rt, ct].float().cpu().numpy(), ref, f"gemm[{M}x{N}x{K}] bf16 sampled")
+
+
+def test_gemm_decode_full():
+    """Decode-shaped: x [32, 7168] with 1% x50 outliers, W [18432, 7168]."""
+    full_size_case(2, 32, 18432, 7168, inputs.seed_for(2, 0), inputs.seed_for(2, 1), outliers=True,
+                   full=True)
+
+
+def test_gemm_prefill_up():
+    full_size_case(3, 4096, 18432, 7168, inputs.seed_for(3, 0), inputs.seed_for(3, 1))
+
+
+def test_gemm_prefill_down():
+    full_size_case(3, 4096, 7168, 18432, inputs.seed_for(3, 2), inputs.seed_for(3, 3))
+
+
+@pytest.mark.parametrize("N,K,tid", [(1536, 7168, 2), (16384, 512, 4)])
+def test_gemm_ue8m0_inputs(N, K, tid):
+    full_size_case(5, 1024, N, K, inputs.seed_for(5, tid), inputs.seed_for(5, tid + 1),
+                   fmt=oracle.FMT_UE8M0)
+
+
+# --------------------------------------------------------------------- MoE
+
+def run_moe(a, a_s, b, b_s, off, out_dtype):
+    c = fp8bs.moe_gemm(to_dev_u8(a), to_dev_f32(a_s), to_dev_u8(b), to_dev_f32(b_s),
+                       torch.from_numpy(off).to(DEV), out_dtype)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([0, 7, 0, 20, 0], 130, 256),
+    ([1, 64, 65, 129, 0, 3], 256, 384),
+    ([300], 200, 128),
+    ([0, 0, 0], 128, 128),
+])
+def test_moe_small(counts, N, K):
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    if R == 0:
+        a = np.zeros((0, K), np.uint8)
+        a_s = np.zeros((0, K // 128), np.float32)
+    else:
+        x = inputs.normal_bf16((R, K), 1.0, 4000 + R)
+        a, a_s = oracle.act_quant(inputs.bf16_bits(x), 0)
+    w = inputs.normal_bf16((E * N, K), 0.02, 5000 + N)
+    bq, bs = [], []
+    for e in range(E):
+        q, s = oracle.weight_quant(inputs.bf16_bits(w[e * N:(e + 1) * N]))
+        bq.append(q)
+        bs.append(s)
+    b, b_s = np.stack(bq), np.stack(bs)
+    if R == 0:                                   # nothing to compute: a no-op launch
+        assert run_moe(a, a_s, b, b_s, off, torch.float32).shape == (0, N)
+        return
+    ref = oracle.moe_gemm(a, a_s, b, b_s, off)
+    assert_close(run_moe(a, a_s, b, b_s, off, torch.float32), ref, f"moe{counts} f32")
+    assert_close(run_moe(a, a_s, b, b_s, off, torch.bfloat16), ref, f"moe{counts} bf16")
+
+
+@pytest.mark.parametrize("proj", ["up", "down"])
+def test_moe_full_size(proj):
+    """The grouped MoE workload: 4096 tokens, 256 experts, top-8 Zipf(1.1)
+    routing; up W [256, 2048, 7168] or down W [256, 7168, 2048].  Weights are
+    drawn on the device (torch generator), quantised by the library, and the
+    quantisation of the experts used below is checked bit-exact against the
+    oracle before their rows are compared."""
+    cfg = inputs.CONFIGS[4]
+    E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
+    N, K = (cfg["up"]["N"], cfg["up"]["K"]) if proj == "up" else (cfg["down"]["N"], cfg["down"]["K"])
+    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    off = route["offsets"]
+    R = int(off[-1])
+    if proj == "up":
+        tok = inputs.normal_bf16((T, K), 1.0, inputs.seed_for(4, 0))
+        x = tok[torch.from_numpy(route["token"])]
+    else:
+        x = inputs.normal_bf16((R, K), 1.0, inputs.seed_for(4, 1))
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), 0)
+    qd, sd = fp8bs.act_quant(x.to(DEV), 0)
+    w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(4, 2 if proj == "up" else 3), DEV)
+    bq, bsq = fp8bs.weight_quant(w)
+    c = fp8bs.moe_gemm(qd, sd, bq.view(E, N, K), bsq.view(E, N // 128, K // 128),
+                       torch.from_numpy(off).to(DEV), torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(qd.view(torch.uint8).cpu().numpy(), a)
+    counts = np.diff(off)
+    pick = sorted({0, int(np.argmax(counts)), int(np.argmin(counts)), E - 1, E // 2,
+                   int(np.argsort(counts)[E // 2])})
+    rng = np.random.default_rng(11)
+    for e in pick:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        we = w[e * N:(e + 1) * N].cpu()
+        be, bse = oracle.weight_quant(inputs.bf16_bits(we))
+        assert np.array_equal(bq[e * N:(e + 1) * N].view(torch.uint8).cpu().numpy(), be)
+        assert np.array_equal(bsq.view(E, N // 128, K // 128)[e].cpu().numpy().view(np.uint32),
+                              bse.view(np.uint32))
+        rows = np.concatenate([np.repeat(np.arange(r0, r1), 3), rng.integers(r0, r1, 2000)])
+        cols = np.concatenate([rng.integers(0, N, 3 * (r1 - r0)), rng.integers(0, N, 2000)])
+        rows = np.concatenate([rows, np.full(N, r0), np.full(N, r1 - 1)])
+        cols = np.concatenate([cols, np.arange(N), np.arange(N)])
+        ref = oracle.gemm_points(a[r0:r1], a_s[r0:r1], be, bse, rows - r0, cols)
+        rt, ct = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+        assert_close(c[rt, ct].cpu().numpy(), ref, f"moe {proj} expert {e} ({r1 - r0} rows)")
