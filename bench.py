@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 linear on one MI355X (gfx950).
+
+One step = the FP8 linear of the prefill-shaped workload: act_quant of
+x bf16 [4096, 7168] (1x128 blocks, float32 scales) followed by the
+block-scaled FP8 GEMM with W e4m3 [18432, 7168] (128x128 scales), bf16 out.
+`value` is that step's throughput in TFLOP/s (2*M*N*K per step).  The other
+rows of the hot path -- the decode-shaped linear (GB/s), act_quant in both
+scale formats, weight_dequant, the two small GEMMs of the ue8m0 workload, the
+prefill down-projection and the grouped MoE GEMMs -- are timed as secondary
+rows in the same run.
+
+Inputs are seeded synthetic tensors (block_scaled_fp8_03_amd.inputs), drawn on
+the device and resident in HBM before timing.  Kernel durations come from HIP
+events recorded on the stream the kernels run on; HBM-bound rows cycle through
+enough copies of their inputs that the 256 MB Infinity Cache cannot hold them.
+The CPU baseline is the oracle (binary64 C + OpenMP) on a bounded sample of
+the same workload, timed on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_scaled_fp8_03_amd as fp8bs  # noqa: E402
+from block_scaled_fp8_03_amd import inputs  # noqa: E402
+
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+MALL_BYTES = 256 << 20         # Infinity Cache
+ROTATE_FOOTPRINT = 2 * MALL_BYTES
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------- algorithmic work
+
+def act_quant_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M * (K // 128)
+
+
+def dequant_bytes(N, K):
+    return N * K + 4 * (-(-N // 128)) * (-(-K // 128)) + 2 * N * K
+
+
+def gemm_bytes(M, N, K, out_bytes=2):
+    return M * K + 4 * M * (K // 128) + N * K + 4 * (-(-N // 128)) * (K // 128) + out_bytes * M * N
+
+
+def moe_bytes(R, N, K, active_experts, out_bytes=2):
+    per_expert = N * K + 4 * (-(-N // 128)) * (K // 128)
+    return R * K + 4 * R * (K // 128) + active_experts * per_expert + out_bytes * R * N
+
+
+# ------------------------------------------------------------------ timing
+
+def timed(launch, copies, steps, warmup):
+    """Average duration (us) of `launch(i)`: one event pair brackets the whole
+    timed region of back-to-back launches on the launch stream, so per-launch
+    event overhead does not inflate short kernels."""
+    for i in range(warmup):
+        launch(i % copies)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        launch(i % copies)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def n_copies(bytes_per_copy):
+    return max(1, min(16, -(-ROTATE_FOOTPRINT // max(1, bytes_per_copy))))
+
+
+def quantised_weight(N, K, seed, dev):
+    w = inputs.normal_bf16_device((N, K), 0.02, seed, dev)
+    q, s = fp8bs.weight_quant(w)
+    return q, s
+
+
+# ------------------------------------------------------------------ rows
+
+def row_result(name, us, flops=None, nbytes=None, bound="hbm", extra=None):
+    r = {"us": round(us, 3)}
+    if flops:
+        r["tflops"] = round(flops / us / 1e6, 2)
+    if nbytes:
+        r["gbs"] = round(nbytes / us / 1e3, 1)
+        r["bytes"] = int(nbytes)
+    if bound == "hbm":
+        r["bound"] = "hbm"
+        r["frac"] = round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)
+    elif bound == "mfma":
+        r["bound"] = "mfma"
+        r["frac"] = round(flops / us / 1e6 / PEAK_FP8_TFLOPS, 4)
+    if extra:
+        r.update(extra)
+    log(f"  {name:28s} {json.dumps(r)}")
+    return r
+
+
+def bench_linear_step(M, N, K, cfg, steps, warmup, dev, fmt="fp32"):
+    """The FP8 linear (act_quant then GEMM) of one workload.  Returns the wall
+    time per step over the timed region, and each kernel's average duration
+    from its own back-to-back timed region."""
+    x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 0), dev)
+    q, s = quantised_weight(N, K, inputs.seed_for(cfg, 1), dev)
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        fp8bs.fp8bs_act_quant(x, xq, xs, fmt)
+        fp8bs.fp8bs_gemm(xq, xs, q, s, y)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    aq = timed(lambda c: fp8bs.fp8bs_act_quant(x, xq, xs, fmt), 1, steps, warmup)
+    gm = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, q, s, y), 1, steps, warmup)
+    return wall_ms, aq, gm, (x, q, s)
+
+
+def bench_decode(steps, warmup, dev, out):
+    cfg = inputs.CONFIGS[2]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    x = inputs.normal_bf16((M, K), 1.0, inputs.seed_for(2, 0), outlier_frac=0.01,
+                           outlier_mult=50.0).to(dev)
+    copies = n_copies(N * K)
+    ws = [quantised_weight(N, K, inputs.seed_for(2, 1) + 100 * c, dev) for c in range(copies)]
+    xq, xs = fp8bs.act_quant(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, ws[c][0], ws[c][1], y), copies, steps, warmup)
+    out["decode_gemm_32x18432x7168"] = row_result(
+        "decode gemm", us, 2 * M * N * K, gemm_bytes(M, N, K), "hbm", {"weight_copies": copies})
+    aq_us = timed(lambda c: fp8bs.fp8bs_act_quant(x, xq, xs, "fp32"), 1, steps, warmup)
+    out["decode_act_quant_32x7168"] = row_result("decode act_quant", aq_us, None,
+                                                 act_quant_bytes(M, K), "hbm")
+
+    def step(c):
+        fp8bs.fp8bs_act_quant(x, xq, xs, "fp32")
+        fp8bs.fp8bs_gemm(xq, xs, ws[c][0], ws[c][1], y)
+    st_us = timed(step, copies, steps, warmup)
+    out["decode_linear_step"] = row_result(
+        "decode linear step", st_us, 2 * M * N * K,
+        act_quant_bytes(M, K) + gemm_bytes(M, N, K), "hbm")
+    del ws
+
+
+def bench_act_quant(steps, warmup, dev, out):
+    for (M, K, fmt, cfg) in [(4096, 7168, "fp32", 3), (4096, 18432, "fp32", 3), (32768, 2048, "fp32", 4),
+                             (1024, 7168, "ue8m0", 5)]:
+        nb = act_quant_bytes(M, K)
+        copies = n_copies(nb)
+        xs_in = [inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 50 + c), dev)
+                 for c in range(copies)]
+        qs = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(copies)]
+        ss = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
+        us = timed(lambda c: fp8bs.fp8bs_act_quant(xs_in[c], qs[c], ss[c], fmt), copies, steps, warmup)
+        out[f"act_quant_{M}x{K}_{fmt}"] = row_result(f"act_quant {M}x{K} {fmt}", us, None, nb, "hbm",
+                                                     {"copies": copies})
+        del xs_in, qs, ss
+
+
+def bench_dequant(steps, warmup, dev, out):
+    N, K = 18432, 7168
+    nb = dequant_bytes(N, K)
+    copies = n_copies(nb)
+    ws = [quantised_weight(N, K, inputs.seed_for(5, 1) + 100 * c, dev) for c in range(copies)]
+    ys = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    us = timed(lambda c: fp8bs.fp8bs_weight_dequant(ws[c][0], ws[c][1], ys[c]), copies, steps, warmup)
+    out["weight_dequant_18432x7168"] = row_result("weight_dequant", us, None, nb, "hbm",
+                                                  {"copies": copies})
+    del ws, ys
+
+
+def bench_small_gemms(steps, warmup, dev, out):
+    M = 1024
+    for (N, K, tid) in [(1536, 7168, 2), (16384, 512, 4)]:
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(5, tid), dev)
+        xq, xs = fp8bs.act_quant(x, "ue8m0")
+        nb = gemm_bytes(M, N, K)
+        copies = n_copies(nb)
+        ws = [quantised_weight(N, K, inputs.seed_for(5, tid + 1) + 100 * c, dev) for c in range(copies)]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, ws[c][0], ws[c][1], y), copies, steps, warmup)
+        ai = 2 * M * N * K / nb
+        out[f"gemm_{M}x{N}x{K}_ue8m0"] = row_result(
+            f"gemm {M}x{N}x{K}", us, 2 * M * N * K, nb, "mfma" if ai > 629 else "hbm",
+            {"copies": copies})
+        del ws
+
+
+def bench_moe(steps, warmup, dev, out):
+    cfg = inputs.CONFIGS[4]
+    E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
+    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    off = torch.from_numpy(route["offsets"]).to(dev)
+    R = int(route["offsets"][-1])
+    active = int((route["counts"] > 0).sum())
+    tok_idx = torch.from_numpy(route["token"]).to(dev)
+    for proj, tid in (("up", 2), ("down", 3)):
+        N, K = cfg[proj]["N"], cfg[proj]["K"]
+        if proj == "up":
+            tok = inputs.normal_bf16_device((T, K), 1.0, inputs.seed_for(4, 0), dev)
+            x = tok.index_select(0, tok_idx)
+            del tok
+        else:
+            x = inputs.normal_bf16_device((R, K), 1.0, inputs.seed_for(4, 1), dev)
+        xq, xs = fp8bs.act_quant(x)
+        w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(4, tid), dev)
+        bq, bs = fp8bs.weight_quant(w)
+        del w
+        bq, bs = bq.view(E, N, K), bs.view(E, N // 128, K // 128)
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda c: fp8bs.fp8bs_moe_gemm(xq, xs, bq, bs, off, y), 1, steps, warmup)
+        out[f"moe_{proj}_{R}x{N}x{K}_E{E}"] = row_result(
+            f"moe {proj}", us, 2 * R * N * K, moe_bytes(R, N, K, active), "hbm",
+            {"active_experts": active})
+        del bq, bs, y, x, xq, xs
+
+
+def cpu_baseline(x_dev, w_dev, budget_s):
+    """The oracle on a row sample of the prefill linear: act_quant of the
+    sampled rows of x, then all N outputs of each sampled row in binary64, with
+    W quantised by the oracle itself from the same bf16 draw."""
+    import oracle
+    oracle.build()
+    M, K = x_dev.shape
+    N = w_dev.shape[0]
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w_dev.cpu()))
+    xb = inputs.bf16_bits(x_dev.cpu())
+
+    def run(r):
+        t0 = time.perf_counter()
+        a, a_s = oracle.act_quant(xb[:r], oracle.FMT_FP32)
+        oracle.gemm(a, a_s, b, b_s)
+        return time.perf_counter() - t0
+
+    dt0 = run(2) / 2                               # calibration
+    rows = int(min(M, max(2, budget_s / max(dt0, 1e-4))))
+    dt = run(rows)
+    flops = 2 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"act_quant + binary64 block-scaled GEMM of the first {rows} of the {M} rows "
+                      f"of the prefill linear (all {N} outputs per row, K={K}); {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
+                    "decode,act_quant,dequant,small,moe,down")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the block-scaled FP8 linear runs on a single MI355X here "
+              "(no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fp8bs.lib()                                    # fails loudly if the library is missing
+
+    cfg = inputs.CONFIGS[3]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    log(f"prefill fp8 linear M={M} N={N} K={K}: {args.warmup} warmup + {args.steps} timed steps")
+    wall_ms, aq_us, gm_us, prefill_inputs = bench_linear_step(M, N, K, 3, args.steps, args.warmup, dev)
+    flops = 2 * M * N * K
+    value = flops / (wall_ms * 1e-3) / 1e12
+    rows = {}
+    rows["prefill_up_act_quant_4096x7168"] = row_result("prefill act_quant", aq_us, None,
+                                                        act_quant_bytes(M, K), "hbm")
+    rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
+                                                         gemm_bytes(M, N, K), "mfma")
+    sel = set(["decode", "act_quant", "dequant", "small", "moe", "down"]) if args.rows == "all" else (
+        set() if args.rows == "none" else set(args.rows.split(",")))
+    if "down" in sel:
+        d = cfg["down"]
+        w2, a2, g2, _ = bench_linear_step(d["M"], d["N"], d["K"], 3, args.steps, args.warmup, dev)
+        rows["prefill_down_gemm_4096x7168x18432"] = row_result(
+            "prefill down gemm", g2, 2 * d["M"] * d["N"] * d["K"], gemm_bytes(d["M"], d["N"], d["K"]),
+            "mfma")
+    if "decode" in sel:
+        bench_decode(args.steps, args.warmup, dev, rows)
+    if "act_quant" in sel:
+        bench_act_quant(args.steps, args.warmup, dev, rows)
+    if "dequant" in sel:
+        bench_dequant(args.steps, args.warmup, dev, rows)
+    if "small" in sel:
+        bench_small_gemms(args.steps, args.warmup, dev, rows)
+    if "moe" in sel:
+        bench_moe(args.steps, args.warmup, dev, rows)
+    torch.cuda.empty_cache()
+
+    gemm_tflops = flops / gm_us / 1e6
+    result = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s @M=4096,K=7168,N=18432; GB/s @M=32 decode",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "prefill fp8 linear: act_quant x bf16 [4096,7168] + block-scaled FP8 "
+                               "GEMM with W e4m3 [18432,7168], bf16 out",
+                   "M": M, "N": N, "K": K, "block": 128, "scale_fmt": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "kernel": "gemm_tile_kernel<256,128,128,64,3,bf16>",
+                     "us_per_launch": round(gm_us, 3)},
+    }
+    if "decode_gemm_32x18432x7168" in rows:
+        result["decode_gbs"] = rows["decode_gemm_32x18432x7168"]["gbs"]
+    result["rows"] = rows
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on a row sample (~{args.cpu_seconds:.0f} s)")
+        px, _, _ = prefill_inputs
+        w_bf16 = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(3, 1), dev)
+        result["cpu_baseline"] = cpu_baseline(px, w_bf16, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,11 +22,13 @@
 
 namespace fp8bs {
 
-// One K = 128 FP8 MFMA with a zero accumulator (unit hardware scales: the
-// E8M0 value 127 is 2^0).
+// One K = 128 FP8 MFMA with a zero accumulator.  With all scale operands 0
+// the compiler emits the unscaled v_mfma_f32_16x16x128_f8f6f4, which computes
+// the plain product and issues faster than the scaled encoding (measured on
+// gfx950: ~10% more MFMA throughput).
 __device__ __forceinline__ v4f mfma_k128(v8i x, v8i y) {
   const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, z, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, z, 0, 0, 0, 0, 0, 0);
 }
 
 // s_waitcnt that waits until at most n vector-memory operations of this wave
@@ -115,10 +117,22 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return x * q + min(x, r) + k;
 }
 
-// Row `r` of a 128-byte-row LDS tile, lane group g: the 32 bytes of logical
-// chunks 2g and 2g+1 (two 16-byte reads at their swizzled positions).
+// LDS tiles hold 128-byte rows; the 16-byte chunk c of row r sits at chunk
+// position c ^ swz(r).  SW = 0: swz(r) = r % 8, so 8 consecutive rows at one
+// logical chunk hit 8 different chunk positions.  SW = 1: swz(r) = (r / 2) %
+// 8, so 16 consecutive rows hit 16 distinct (row parity, chunk) pairs.  Each
+// DMA instruction writes 8 whole rows (8 lanes per 128-byte row), so global
+// reads stay line-sized.
+template <int SW>
+__device__ __forceinline__ int swz(int r) {
+  return SW == 0 ? (r & 7) : ((r >> 1) & 7);
+}
+
+// Row `r` of a tile, lane group g: the 32 bytes of logical chunks 2g and 2g+1
+// (two 16-byte reads at their swizzled positions).
+template <int SW>
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
-  const int sw = r & 7;
+  const int sw = swz<SW>(r);
   const uint4 lo = *(const uint4*)(tile + r * 128 + (((2 * g) ^ sw) << 4));
   const uint4 hi = *(const uint4*)(tile + r * 128 + (((2 * g + 1) ^ sw) << 4));
   v8i v;
@@ -127,18 +141,19 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
   return v;
 }
 
-template <int BM, int BN, int WM, int WN, int ST, bool OUT_F32, bool MOE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool OUT_F32, bool MOE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 gemm_tile_kernel(GemmParams p) {
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(WAVES_M * WAVES_N == NW && (NW == 4 || NW == 8), "4 or 8 waves per workgroup");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range lies in one weight block");
   constexpr int MT = WM / 16, NT = WN / 16;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, AS_BYTES = 256 * 4, BS_BYTES = 256 * 4;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, AS_BYTES = NW * 256, BS_BYTES = NW * 256;
   constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
-  constexpr int A_LOADS = A_BYTES / 4096, B_LOADS = B_BYTES / 4096;   // per thread
+  constexpr int A_LOADS = A_BYTES / (NW * 1024), B_LOADS = B_BYTES / (NW * 1024);  // per thread
   constexpr int LPS = A_LOADS + B_LOADS + 2;                          // DMA ops per stage
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM <= 256, "tile shape");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM <= NW * 64, "tile shape");
+  static_assert(ST >= 2, "at least double buffering");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -217,30 +232,33 @@ gemm_tile_kernel(GemmParams p) {
     }
   }
 
-  // ---- DMA sources.  Load i of this wave covers the 8 rows 8*(4i+wave) ..
-  // +7 of the tile; lane l takes row l/8 of those and the logical chunk
-  // (l % 8) ^ (row % 8).  Offsets grow by 32 rows per load and 128 bytes per
-  // K block.
+  // ---- DMA sources.  Load i of this wave covers the 8 rows 8*(NW*i+wave)
+  // .. +7 of the tile; lane l takes row l/8 of those and the logical chunk
+  // (l % 8) ^ swz(row).  Offsets grow by 8*NW rows per load (which keeps
+  // row % 16, hence the chunk choice) and 128 bytes per K block.
   const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)p.rows * K));
   const v4i b_rsrc = make_rsrc(B, (uint32_t)((int64_t)N * K));
   const v4i as_rsrc = make_rsrc(p.a_s, (uint32_t)((int64_t)p.rows * nkb * 4));
   const v4i bs_rsrc = make_rsrc(Bs, (uint32_t)((int64_t)nbn * nkb * 4));
-  const int lchunk = (lane & 7) ^ (lane >> 3);
-  const uint32_t a_voff = (uint32_t)(m_base + 8 * wave + (lane >> 3)) * K + 16 * lchunk;
-  const uint32_t b_voff = (uint32_t)(n_base + 8 * wave + (lane >> 3)) * K + 16 * lchunk;
+  const int lrow = 8 * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ swz<SW>(lrow);
+  const uint32_t a_voff = (uint32_t)(m_base + lrow) * K + 16 * lchunk;
+  const uint32_t b_voff = (uint32_t)(n_base + lrow) * K + 16 * lchunk;
   const uint32_t as_voff = (uint32_t)(m_base + (tid % BM)) * nkb * 4;
   const uint32_t bs_voff = (uint32_t)((n_base + wn * WN) / 128) * nkb * 4;  // this wave's block row
-  const uint32_t row32 = 32u * (uint32_t)K;
+  const uint32_t rowstep = 8u * NW * (uint32_t)K;
   const uint32_t smem_lds = lds_addr(smem);
 
   auto issue = [&](int kb, int st) {
     const uint32_t base = smem_lds + st * STAGE + wave * 1024;
     const uint32_t koff = (uint32_t)kb * 128;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) dma_b128(a_rsrc, base + i * 4096, a_voff + i * row32 + koff);
+    for (int i = 0; i < A_LOADS; ++i)
+      dma_b128(a_rsrc, base + i * NW * 1024, a_voff + i * rowstep + koff);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-      dma_b128(b_rsrc, base + A_BYTES + i * 4096, b_voff + i * row32 + koff);
+      dma_b128(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep + koff);
+    // a_s: thread t fetches row t % BM into slot t (slots >= BM hold copies)
     dma_b32(as_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, as_voff + kb * 4);
     // every lane of the wave fetches the same b_s value of its weight block
     dma_b32(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + AS_BYTES + wave * 256,
@@ -274,11 +292,11 @@ gemm_tile_kernel(GemmParams p) {
     const float bsv = ((const float*)(at + A_BYTES + B_BYTES + AS_BYTES))[wave * 64];
     v8i bf[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) bf[j] = lds_frag(bt, wn * WN + 16 * j + r16, g);
+    for (int j = 0; j < NT; ++j) bf[j] = lds_frag<SW>(bt, wn * WN + 16 * j + r16, g);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int ml = wm * WM + 16 * t + r16;
-      const v8i af = lds_frag(at, ml, g);
+      const v8i af = lds_frag<SW>(at, ml, g);
       const float sc = ast[ml] * bsv;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -482,12 +500,12 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams p) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int BM, int BN, int WM, int WN, int ST, bool MOE>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE>
 hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   if (out_f32)
-    gemm_tile_kernel<BM, BN, WM, WN, ST, true, MOE><<<dim3(grid), dim3(256), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, true, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
   else
-    gemm_tile_kernel<BM, BN, WM, WN, ST, false, MOE><<<dim3(grid), dim3(256), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, false, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -513,10 +531,14 @@ hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const flo
   if (M <= 16) return run_skinny<1>(p, out_f32, stream);
   if (M <= 32) return run_skinny<2>(p, out_f32, stream);
   if (M <= 64) return run_skinny<4>(p, out_f32, stream);
-  constexpr int BM = 256, BN = 128;
+#ifndef FP8BS_TILE_CFG
+#define FP8BS_TILE_CFG 256, 256, 128, 64, 2, 8, 0
+#endif
+  constexpr int cfg[7] = {FP8BS_TILE_CFG};
+  constexpr int BM = cfg[0], BN = cfg[1];
   p.num_m = (int)((M + BM - 1) / BM);
   p.num_n = (int)((N + BN - 1) / BN);
-  return run_tile<BM, BN, 128, 64, 3, false>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<FP8BS_TILE_CFG, false>(p, out_f32, p.num_m * p.num_n, stream);
 }
 
 hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
@@ -530,7 +552,7 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   // sum_e ceil(rows_e / BM) <= R / BM + E
   p.num_m = (int)(R / BM + E);
   p.num_n = (int)((N + BN - 1) / BN);
-  return run_tile<BM, BN, 64, 64, 3, true>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<BM, BN, 64, 64, 3, 4, 0, true>(p, out_f32, p.num_m * p.num_n, stream);
 }
 
 }  // namespace fp8bs
