@@ -276,6 +276,9 @@ def main():
                     "decode,act_quant,dequant,small,moe,down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (known traffic) so hardware byte "
+                         "counters collected over this run can be scaled against it")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -288,6 +291,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fp8bs.lib()                                    # fails loudly if the library is missing
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = inputs.CONFIGS[3]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
