@@ -17,6 +17,8 @@
 // whichever 32 bytes each lane group carries, as long as both operands use
 // the same choice, so lane group g carries K bytes [32g, 32g + 32).  The
 // result lane l, register r is D[4 (l / 16) + r][l % 16].
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -345,23 +347,18 @@ gemm_tile_kernel(GemmParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// Skinny kernel (M <= 64): weight streaming for decode-shaped products.
+// Helpers for the HBM-bound decode kernel
 // ----------------------------------------------------------------------------
-// A workgroup owns 16*NTW rows of B (weights) and all M rows of A.  Its four
-// waves split the K blocks round-robin (wave w takes kb = w, w+4, ...), each
-// streaming its weight fragments straight from HBM into VGPRs (no LDS: no
-// operand is shared between waves), D K blocks in flight per wave.  The four
-// partial accumulators are summed through LDS at the end.
-//
-// Arithmetic.  The FP8 MFMA sums its 128 products in a reduced-precision
-// internal format (measured on gfx950: errors up to ~1.4e-5 of the sum of
-// |products| on normal data and ~2.3e-4 with 50x outliers), while the bf16
-// MFMA on the same values is accurate to ~2e-8.  This kernel is bound by HBM,
-// not by the matrix cores, so it decodes the e4m3 bytes to bf16 in registers
-// (exact: every e4m3 value is a bf16 value) and runs four K = 32 bf16 MFMAs
-// per 128-wide K block; the block's partial is then scaled and added in fp32
-// as in the tile kernel.  K mapping: instruction i, lane group g takes the
-// bytes [32g + 8i, 32g + 8i + 8) of the block for both operands.
+// bf16 MFMA on decoded e4m3 operands.  The FP8 MFMA sums its 128 products in
+// a reduced-precision internal format (measured on gfx950: errors up to
+// ~1.4e-5 of the sum of |products| on normal data and ~2.3e-4 with 50x
+// outliers), while the bf16 MFMA on the same values is accurate to ~2e-8.
+// The decode kernel is bound by HBM, not by the matrix cores, so it decodes
+// the e4m3 bytes to bf16 in registers (exact: every e4m3 value is a bf16
+// value) and runs four K = 32 bf16 MFMAs per 128-wide K block; the block's
+// partial is then scaled and added in fp32 as in the tile kernel.  K mapping:
+// instruction i, lane group g takes the bytes [32g + 8i, 32g + 8i + 8) of the
+// block for both operands.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
@@ -375,50 +372,91 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-template <int MT, int NTW, int D, bool OUT_F32>
-__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// ----------------------------------------------------------------------------
+// Decode kernel (M <= 16*MT): HBM-bound weight streaming through LDS.
+// ----------------------------------------------------------------------------
+// One workgroup per CU: workgroup g owns the `rows` (a multiple of 8, at most
+// 80) consecutive weight rows starting at g*rows, chosen on the host so the
+// rows are spread evenly over the CUs, plus all M (<= 16*MT) activation rows.
+// Each LDS stage holds KPS = 2 consecutive K blocks of both operands, filled
+// by direct buffer->LDS loads whose every wave instruction covers 8 rows x one
+// whole 128-byte line; the two K blocks of the same 8 rows are issued back to
+// back, so each row is read 256 contiguous bytes at a time (the access pattern
+// that streamed fastest on gfx950).  Five stages (~145 KB for M <= 32) keep
+// four stages -- ~73 KB of weights per CU -- in flight.  Row groups past
+// `rows` are requested at an out-of-range offset, which the buffer unit
+// returns as zeros without touching memory.
+// Wave w computes K block (w % 2) of every stage for the three 16-row tiles
+// 3 (w / 2) .. 3 (w / 2) + 2 (tiles past `rows` read unused LDS and are never
+// stored); the two waves of a pair are summed through LDS at the end.
+// Arithmetic: e4m3 decoded to bf16, four K = 32 bf16 MFMAs per K block, one
+// scale fold per K block in fp32 (see the helpers above).
+constexpr int kDecodeMaxRows = 80;
+
+template <int MT, bool OUT_F32>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_decode_kernel(GemmParams p, int rows) {
+  constexpr int NW = 4, KPS = 2, MR = 16 * MT;
+  constexpr int ST = MT <= 2 ? 5 : 3;
+  constexpr int OCT = kDecodeMaxRows / 8;                        // row groups per K block
+  constexpr int B_TILE = kDecodeMaxRows * 128, A_TILE = MR * 128;  // one K block
+  constexpr int B_BYTES = KPS * B_TILE, A_BYTES = KPS * A_TILE;
+  constexpr int AS_BYTES = NW * 256, BS_BYTES = NW * 256;
+  constexpr int STAGE = B_BYTES + A_BYTES + AS_BYTES + BS_BYTES;
+  constexpr int B_LOADS = KPS * OCT / NW, A_LOADS = A_BYTES / (NW * 1024);
+  constexpr int LPS = B_LOADS + A_LOADS + 2;
+  constexpr int NTW = 3;                                          // tiles per wave
+  static_assert((KPS * OCT) % NW == 0 && A_LOADS >= 1 && MR <= 64, "shape");
+  static_assert(ST * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int M = p.rows, N = p.N, K = p.K;
-  const int nkb = K / 128;
-  const int n_base = blockIdx.x * (16 * NTW);
-  // Every wave's n rows lie in one weight block only if 16*NTW divides 128.
-  static_assert(128 % (16 * NTW) == 0, "weight block alignment");
-  const int bs_row = n_base / 128;
+  const int nkb = K / 128, nkc = (nkb + KPS - 1) / KPS;
+  const int n_base = blockIdx.x * rows;
+  const int n_end = min(n_base + rows, N);
+  const int q = wave & 1;                                 // this wave's K block in a stage
+  const int jt0 = NTW * (wave >> 1);                      // this wave's first tile
 
-  // byte offsets of this lane's operand rows (clamped inside the matrices)
-  int64_t b_row_off[NTW], a_row_off[MT];
-  int a_s_row[MT];
+  const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)M * K));
+  const v4i b_rsrc = make_rsrc(p.b, (uint32_t)((int64_t)N * K));
+  const v4i as_rsrc = make_rsrc(p.a_s, (uint32_t)((int64_t)M * nkb * 4));
+  const int nbn = (N + 127) / 128;
+  const v4i bs_rsrc = make_rsrc(p.b_s, (uint32_t)((int64_t)nbn * nkb * 4));
+  // DMA instruction u = NW i + wave covers row group u / KPS of K block
+  // u % KPS = q; lane l takes row l / 8 of the group and logical chunk
+  // (l % 8) ^ (l / 8) (the row's swizzle, row % 8 = l / 8).
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  const int grp0 = wave >> 1;                             // row group of i = 0; +2 per i
+  uint32_t b_voff[B_LOADS];
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) b_row_off[j] = (int64_t)min(n_base + 16 * j + r16, N - 1) * K + 32 * g;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int m = min(16 * t + r16, M - 1);
-    a_row_off[t] = (int64_t)m * K + 32 * g;
-    a_s_row[t] = m * nkb;
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int grp = grp0 + 2 * i;
+    b_voff[i] = 8 * grp < rows
+                    ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * q
+                    : 0xF0000000u;                       // past the buffer: zeros
   }
+  const uint32_t a_voff = (uint32_t)(8 * grp0 + (lane >> 3)) * K + 16 * lchunk + 128 * q;
+  const uint32_t as_voff = (uint32_t)lane * nkb * 4 + 4 * q;       // lane = activation row
+  // lanes 0 and 1 fetch the scales of the (at most two) weight blocks the
+  // workgroup's rows touch
+  const uint32_t bs_voff = (uint32_t)(n_base / 128 + (lane & 1)) * nkb * 4 + 4 * q;
+  const uint32_t step16 = 16u * (uint32_t)K;              // 2 row groups per i
+  const uint32_t smem_lds = lds_addr(smem);
 
-  typedef unsigned v4u __attribute__((ext_vector_type(4)));
-  struct Slot {
-    v4u b[NTW][2];
-    v4u a[MT][2];
-    float as[MT];
-  };
-  auto load = [&](Slot& s, int kb) {
+  auto issue = [&](int kc, int st) {
+    const uint32_t base = smem_lds + st * STAGE;
+    const uint32_t koff = (uint32_t)kc * (KPS * 128);
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      // weights are read exactly once: non-temporal loads keep them out of L2
-      const v4u* src = (const v4u*)(p.b + b_row_off[j] + (int64_t)kb * 128);
-      s.b[j][0] = __builtin_nontemporal_load(src);
-      s.b[j][1] = __builtin_nontemporal_load(src + 1);
-    }
+    for (int i = 0; i < B_LOADS; ++i)
+      dma_b128(b_rsrc, base + q * B_TILE + (grp0 + 2 * i) * 1024, b_voff[i] + koff);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const v4u* src = (const v4u*)(p.a + a_row_off[t] + (int64_t)kb * 128);
-      s.a[t][0] = src[0];
-      s.a[t][1] = src[1];
-      s.as[t] = p.a_s[a_s_row[t] + kb];
-    }
+    for (int i = 0; i < A_LOADS; ++i)
+      dma_b128(a_rsrc, base + B_BYTES + q * A_TILE + (grp0 + 2 * i) * 1024, a_voff + i * step16 + koff);
+    dma_b32(as_rsrc, base + B_BYTES + A_BYTES + wave * 256, as_voff + kc * (KPS * 4));
+    dma_b32(bs_rsrc, base + B_BYTES + A_BYTES + AS_BYTES + wave * 256, bs_voff + kc * (KPS * 4));
   };
 
   v4f acc[NTW][MT];
@@ -427,70 +465,90 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const Slot& s, int kb) {
-    const float bsv = p.b_s[(int64_t)bs_row * nkb + kb];
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nkc) issue(s, s);
+
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int st = kc % ST;
+    if (kc + ST - 2 < nkc) wait_vmcnt<(ST - 2) * LPS>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (kc + ST - 1 < nkc) issue(kc + ST - 1, (kc + ST - 1) % ST);
+    if (kc * KPS + q >= nkb) continue;                   // odd tail: no second K block
+    const uint8_t* base = smem + st * STAGE;
+    const uint8_t* bt = base + q * B_TILE;
+    const uint8_t* at = base + B_BYTES + q * A_TILE;
+    const float* ast = (const float*)(base + B_BYTES + A_BYTES + wave * 256);
+    const float* bst = (const float*)(base + B_BYTES + A_BYTES + AS_BYTES + wave * 256);
     v8bf af[MT][4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int t = 0; t < MT; ++t) {
+      const v8i f = lds_frag<0>(at, 16 * t + r16, g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[t][i] = e4m3x8_to_bf16(s.a[t][i / 2][2 * (i % 2)], s.a[t][i / 2][2 * (i % 2) + 1]);
+      for (int i = 0; i < 4; ++i) af[t][i] = e4m3x8_to_bf16(f[2 * i], f[2 * i + 1]);
+    }
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
+      // rows of tile jt0 + j past the B region read the A region (unused results)
+      const v8i f = lds_frag<0>(bt, 16 * (jt0 + j) + r16, g);
+      // this lane's four rows share one weight block
+      const int nl = n_base + 16 * (jt0 + j) + 4 * g;
+      const float bsv = bst[(nl / 128 - n_base / 128) & 1];
       v8bf bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bf[i] = e4m3x8_to_bf16(s.b[j][i / 2][2 * (i % 2)], s.b[j][i / 2][2 * (i % 2) + 1]);
+      for (int i = 0; i < 4; ++i) bf[i] = e4m3x8_to_bf16(f[2 * i], f[2 * i + 1]);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         v4f pr = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], af[t][i], pr, 0, 0, 0);
-        const float sc = s.as[t] * bsv;
+        const float sc = ast[16 * t + r16] * bsv;
         acc[j][t][0] = __builtin_fmaf(pr[0], sc, acc[j][t][0]);
         acc[j][t][1] = __builtin_fmaf(pr[1], sc, acc[j][t][1]);
         acc[j][t][2] = __builtin_fmaf(pr[2], sc, acc[j][t][2]);
         acc[j][t][3] = __builtin_fmaf(pr[3], sc, acc[j][t][3]);
       }
     }
-  };
-
-  // this wave's K blocks: kb = wave + 4 i, i < cnt
-  const int cnt = nkb > wave ? (nkb - wave + 3) / 4 : 0;
-  Slot ring[D];
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d)
-    if (d < cnt) load(ring[d], wave + 4 * d);
-  for (int i0 = 0; i0 < cnt; i0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int i = i0 + d;
-      if (i < cnt) {
-        if (i + D - 1 < cnt) load(ring[(d + D - 1) % D], wave + 4 * (i + D - 1));
-        compute(ring[d], wave + 4 * i);
-      }
-    }
   }
 
-  // ---- cross-wave reduction through LDS, then store
-  constexpr int NV = NTW * MT * 4;                 // values per lane
-  __shared__ float red[4][NV][64];
+  // ---- pairwise reduction (waves w and w ^ 1 hold the same tiles), store
+  constexpr int NV = NTW * MT * 4;
+  float* red = (float*)smem;                             // [NW][NV][64], reused
+  barrier_lds();
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][(j * MT + t) * 4 + r][lane] = acc[j][t][r];
-  __syncthreads();
-  for (int idx = tid; idx < NV * 64; idx += 256) {
-    const int v = idx / 64, l = idx % 64;
-    const float sum = red[0][v][l] + red[1][v][l] + red[2][v][l] + red[3][v][l];
-    const int r = v % 4, jt = v / 4, t = jt % MT, j = jt / MT;
-    const int m = 16 * t + (l & 15);
-    const int n = n_base + 16 * j + 4 * (l >> 4) + r;
-    if (m < M && n < N) {
-      if (OUT_F32) ((float*)p.c)[(int64_t)m * N + n] = sum;
-      else ((uint16_t*)p.c)[(int64_t)m * N + n] = (uint16_t)(pack2_bf16(sum, 0.0f) & 0xFFFFu);
+      for (int r = 0; r < 4; ++r) red[(wave * NV + (j * MT + t) * 4 + r) * 64 + lane] = acc[j][t][r];
+  barrier_lds();
+  if (q == 0) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int n = n_base + 16 * (jt0 + j) + 4 * g;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int m = 16 * t + r16;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[r] = acc[j][t][r] + red[((wave + 1) * NV + (j * MT + t) * 4 + r) * 64 + lane];
+        if (m >= M || n >= n_end) continue;
+        if (OUT_F32) {
+          float* cp = (float*)p.c + (int64_t)m * N + n;
+          if ((N % 4) == 0 && n + 3 < n_end) *(float4*)cp = make_float4(v[0], v[1], v[2], v[3]);
+          else for (int r = 0; r < 4; ++r) if (n + r < n_end) cp[r] = v[r];
+        } else {
+          uint16_t* cp = (uint16_t*)p.c + (int64_t)m * N + n;
+          const uint32_t lo = pack2_bf16(v[0], v[1]), hi = pack2_bf16(v[2], v[3]);
+          if ((N % 4) == 0 && n + 3 < n_end) *(uint2*)cp = make_uint2(lo, hi);
+          else {
+            const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+            for (int r = 0; r < 4; ++r) if (n + r < n_end) cp[r] = h[r];
+          }
+        }
+      }
     }
   }
 }
@@ -509,14 +567,31 @@ hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t str
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 template <int MT>
-hipError_t run_skinny(const GemmParams& p, bool out_f32, hipStream_t stream) {
-  constexpr int NTW = 4, D = 3;
-  const int grid = (p.N + 16 * NTW - 1) / (16 * NTW);
+hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
+  // rows per workgroup: a multiple of 8 that spreads N over the CUs, at most 80
+  const int cus = device_cus();
+  const int groups = (p.N + 7) / 8;
+  const int rows = 8 * std::min(kDecodeMaxRows / 8, (groups + cus - 1) / cus);
+  const int grid = (p.N + rows - 1) / rows;
   if (out_f32)
-    gemm_skinny_kernel<MT, NTW, D, true><<<dim3(grid), dim3(256), 0, stream>>>(p);
+    gemm_decode_kernel<MT, true><<<dim3(grid), dim3(256), 0, stream>>>(p, rows);
   else
-    gemm_skinny_kernel<MT, NTW, D, false><<<dim3(grid), dim3(256), 0, stream>>>(p);
+    gemm_decode_kernel<MT, false><<<dim3(grid), dim3(256), 0, stream>>>(p, rows);
   return hipGetLastError();
 }
 
@@ -528,9 +603,9 @@ hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const flo
   GemmParams p{};
   p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
   p.offsets = nullptr; p.rows = (int)M; p.N = (int)N; p.K = (int)K; p.E = 0;
-  if (M <= 16) return run_skinny<1>(p, out_f32, stream);
-  if (M <= 32) return run_skinny<2>(p, out_f32, stream);
-  if (M <= 64) return run_skinny<4>(p, out_f32, stream);
+  if (M <= 16) return run_decode<1>(p, out_f32, stream);
+  if (M <= 32) return run_decode<2>(p, out_f32, stream);
+  if (M <= 64) return run_decode<4>(p, out_f32, stream);
 #ifndef FP8BS_TILE_CFG
 #define FP8BS_TILE_CFG 256, 256, 128, 64, 2, 8, 0
 #endif
