@@ -90,11 +90,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 //   stage = [A tile BM x 128 bytes][B tile BN x 128 bytes][a_s column, 256 floats]
 //           [b_s of each wave's weight block, 4 x 64 floats]
 // filled by direct buffer->LDS loads, so no VGPRs are spent on staging.
-// Rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-// position c ^ (r % 8), which spreads both the DMA writes (8 rows x 8 chunks
-// per wave instruction) and the MFMA operand reads (8 rows x one chunk per 8
-// lanes) over all LDS banks.  Rows past the end of an operand read as zeros
-// (buffer range check) and their results are never stored.
+// Rows are 128 bytes, their 16-byte chunks permuted by an XOR swizzle of the
+// row index (below) so the MFMA operand reads are free of bank conflicts.
+// Rows past the end of an operand read as zeros (buffer range check) and
+// their results are never stored.
 
 struct GemmParams {
   const uint8_t* a;       // [rows, K] e4m3
@@ -120,14 +119,20 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 }
 
 // LDS tiles hold 128-byte rows; the 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r).  SW = 0: swz(r) = r % 8, so 8 consecutive rows at one
-// logical chunk hit 8 different chunk positions.  SW = 1: swz(r) = (r / 2) %
-// 8, so 16 consecutive rows hit 16 distinct (row parity, chunk) pairs.  Each
-// DMA instruction writes 8 whole rows (8 lanes per 128-byte row), so global
-// reads stay line-sized.
+// position c ^ swz(r).  Measured on gfx950, a ds_read_b128 is served in four
+// cycles of 16 lanes -- the lanes of one half-wave with equal parity of lane
+// bits 2..4 -- over 64 four-byte banks (one cycle per 256 bytes), so a cycle
+// is conflict-free when its 16 lanes touch 16 distinct 16-byte positions
+// modulo 256 bytes.  In the MFMA operand read, lane l takes row l % 16 and
+// chunk 2 (l / 16) (+1), and
+//   SW = 2: swz(r) = r1 | r2 << 2 (bits of r)
+// makes every cycle conflict-free.  SW = 0 (swz(r) = r % 8) and SW = 1
+// (swz(r) = (r / 2) % 8) leave two-way conflicts.  Each DMA instruction
+// writes 8 whole rows (8 lanes per 128-byte row, contiguous in LDS), so
+// global reads stay line-sized whatever the swizzle.
 template <int SW>
 __device__ __forceinline__ int swz(int r) {
-  return SW == 0 ? (r & 7) : ((r >> 1) & 7);
+  return SW == 0 ? (r & 7) : SW == 1 ? ((r >> 1) & 7) : (((r >> 1) & 1) | (r & 4));
 }
 
 // Row `r` of a tile, lane group g: the 32 bytes of logical chunks 2g and 2g+1
@@ -607,7 +612,7 @@ hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const flo
   if (M <= 32) return run_decode<2>(p, out_f32, stream);
   if (M <= 64) return run_decode<4>(p, out_f32, stream);
 #ifndef FP8BS_TILE_CFG
-#define FP8BS_TILE_CFG 256, 256, 128, 64, 2, 8, 0
+#define FP8BS_TILE_CFG 256, 256, 128, 64, 2, 8, 2
 #endif
   constexpr int cfg[7] = {FP8BS_TILE_CFG};
   constexpr int BM = cfg[0], BN = cfg[1];
@@ -627,7 +632,7 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   // sum_e ceil(rows_e / BM) <= R / BM + E
   p.num_m = (int)(R / BM + E);
   p.num_n = (int)((N + BN - 1) / BN);
-  return run_tile<BM, BN, 64, 64, 3, 4, 0, true>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<BM, BN, 64, 64, 3, 4, 2, true>(p, out_f32, p.num_m * p.num_n, stream);
 }
 
 }  // namespace fp8bs
