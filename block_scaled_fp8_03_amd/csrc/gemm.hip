@@ -148,20 +148,36 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
   return v;
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool OUT_F32, bool MOE>
+// Activation scales.  With ASCH = false each stage carries the tile's a_s
+// column for its K block, fetched as one float per row: a 64-byte memory
+// request per row and K block.  With ASCH = true (needs K/128 % 4 == 0 and a
+// 16-byte aligned a_s) the scales come in chunks of ASC = NW*256/BM
+// consecutive K blocks, BM rows x ASC floats, loaded 16 bytes per lane
+// (ASC/4 lanes per row) into one of two LDS chunk buffers.  Chunk c is issued
+// together with the DMA of stage ASC*c, so it is complete whenever that stage
+// is; it overwrites chunk c-2, whose last K block ASC*(c-1)-1 is finished by
+// every wave once the barrier before that issue has passed (ASC >= ST - 1).
+// Stages that start no chunk issue an out-of-range dummy load (no memory
+// traffic) when ST > 2 so that every stage has the same number of DMA ops.
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool MOE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 gemm_tile_kernel(GemmParams p) {
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static_assert(WAVES_M * WAVES_N == NW && (NW == 4 || NW == 8), "4 or 8 waves per workgroup");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range lies in one weight block");
   constexpr int MT = WM / 16, NT = WN / 16;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, AS_BYTES = NW * 256, BS_BYTES = NW * 256;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, BS_BYTES = NW * 256;
+  constexpr int AS_BYTES = ASCH ? 0 : NW * 256;
   constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
   constexpr int A_LOADS = A_BYTES / (NW * 1024), B_LOADS = B_BYTES / (NW * 1024);  // per thread
   constexpr int LPS = A_LOADS + B_LOADS + 2;                          // DMA ops per stage
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM <= NW * 64, "tile shape");
   static_assert(ST >= 2, "at least double buffering");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
+  constexpr int ASC = ASCH ? NW * 256 / BM : 1;                       // K blocks per a_s chunk
+  static_assert(!ASCH || (ASC % 4 == 0 && ASC >= ST - 1), "a_s chunk shape");
+  constexpr int CHUNK_BYTES = ASCH ? NW * 1024 : 0;
+  constexpr int DUMMY_BYTES = (ASCH && ST > 2) ? 256 : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 2 * CHUNK_BYTES + DUMMY_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -255,6 +271,14 @@ gemm_tile_kernel(GemmParams p) {
   const uint32_t bs_voff = (uint32_t)((n_base + wn * WN) / 128) * nkb * 4;  // this wave's block row
   const uint32_t rowstep = 8u * NW * (uint32_t)K;
   const uint32_t smem_lds = lds_addr(smem);
+  // a_s chunk piece of this lane: row (64 wave + lane) / (ASC/4), K blocks
+  // 4 ((64 wave + lane) % (ASC/4)) .. +3 of the chunk; lands at byte
+  // 16 (64 wave + lane) of the chunk buffer, i.e. row-major [BM][ASC].
+  constexpr int LPR = ASCH ? ASC / 4 : 1;                              // lanes per a_s row
+  const int as_idx = 64 * wave + lane;
+  const uint32_t asc_voff = ((uint32_t)(m_base + as_idx / LPR) * nkb + 4 * (as_idx % LPR)) * 4;
+  const uint32_t chunk_lds = smem_lds + ST * STAGE + wave * 1024;
+  const uint32_t dummy_lds = smem_lds + ST * STAGE + 2 * CHUNK_BYTES;
 
   auto issue = [&](int kb, int st) {
     const uint32_t base = smem_lds + st * STAGE + wave * 1024;
@@ -265,8 +289,15 @@ gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
       dma_b128(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep + koff);
-    // a_s: thread t fetches row t % BM into slot t (slots >= BM hold copies)
-    dma_b32(as_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, as_voff + kb * 4);
+    if (ASCH) {
+      if (kb % ASC == 0)
+        dma_b128(as_rsrc, chunk_lds + ((kb / ASC) & 1) * CHUNK_BYTES, asc_voff + kb * 4);
+      else if (ST > 2)
+        dma_b32(as_rsrc, dummy_lds, 0xF0000000u);
+    } else {
+      // a_s: thread t fetches row t % BM into slot t (slots >= BM hold copies)
+      dma_b32(as_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, as_voff + kb * 4);
+    }
     // every lane of the wave fetches the same b_s value of its weight block
     dma_b32(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + AS_BYTES + wave * 256,
             bs_voff + kb * 4);
@@ -295,7 +326,9 @@ gemm_tile_kernel(GemmParams p) {
 
     const uint8_t* at = smem + st * STAGE;
     const uint8_t* bt = at + A_BYTES;
-    const float* ast = (const float*)(at + A_BYTES + B_BYTES);
+    const float* ast = ASCH ? (const float*)(smem + ST * STAGE + ((kb / ASC) & 1) * CHUNK_BYTES)
+                            : (const float*)(at + A_BYTES + B_BYTES);
+    const int as_col = ASCH ? kb % ASC : 0;
     const float bsv = ((const float*)(at + A_BYTES + B_BYTES + AS_BYTES))[wave * 64];
     v8i bf[NT];
 #pragma unroll
@@ -304,7 +337,7 @@ gemm_tile_kernel(GemmParams p) {
     for (int t = 0; t < MT; ++t) {
       const int ml = wm * WM + 16 * t + r16;
       const v8i af = lds_frag<SW>(at, ml, g);
-      const float sc = ast[ml] * bsv;
+      const float sc = ast[ml * ASC + as_col] * bsv;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const v4f pr = mfma_k128(bf[j], af);
@@ -563,12 +596,23 @@ gemm_decode_kernel(GemmParams p, int rows) {
 // ----------------------------------------------------------------------------
 namespace {
 
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool MOE>
+void launch_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
+  if (out_f32)
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+  else
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+}
+
+// Chunked a_s loads (16 bytes per lane) need every row of a_s to start on a
+// 16-byte boundary.
 template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE>
 hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
-  if (out_f32)
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, true, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+  const bool chunked = (p.K / 128) % 4 == 0 && ((uintptr_t)p.a_s & 15) == 0;
+  if (chunked)
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, MOE>(p, out_f32, grid, stream);
   else
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, false, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, MOE>(p, out_f32, grid, stream);
   return hipGetLastError();
 }
 

@@ -41,7 +41,24 @@ def run_gemm(a, a_s, b, b_s, out_dtype):
 
 
 SMALL = [(16, 256, 256), (1, 1, 128), (5, 7, 128), (33, 130, 256), (64, 64, 128),
-         (65, 200, 384), (257, 129, 256), (300, 520, 1024), (512, 384, 640), (2, 300, 7168)]
+         (65, 200, 384), (257, 129, 256), (300, 520, 1024), (512, 384, 640), (2, 300, 7168),
+         (257, 300, 1536), (520, 260, 3072)]
+
+
+def test_gemm_unaligned_scales():
+    """a_s starting 4 bytes past a 16-byte boundary: the kernel must then
+    read the activation scales one float at a time (K/128 is a multiple of 4
+    here, so an aligned a_s would be read in 16-byte pieces)."""
+    M, N, K = 300, 260, 1536
+    a, a_s, b, b_s = rand_operands(M, N, K, 3999)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    buf = torch.empty(a_s.size + 4, dtype=torch.float32, device=DEV)
+    a_s_dev = buf[1:1 + a_s.size].view(M, K // 128)
+    a_s_dev.copy_(torch.from_numpy(a_s))
+    assert a_s_dev.data_ptr() % 16 == 4
+    c = fp8bs.fp8_gemm(to_dev_u8(a), a_s_dev, to_dev_u8(b), to_dev_f32(b_s), torch.float32)
+    torch.cuda.synchronize()
+    assert_close(c.float().cpu().numpy(), ref, "gemm unaligned a_s")
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
