@@ -42,6 +42,15 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 << 20         # Infinity Cache
 ROTATE_FOOTPRINT = 2 * MALL_BYTES
 
+# The prefill GEMM kernel: tile 256x256, 128x64 per wave, 2 LDS stages, 8 waves,
+# conflict-free swizzle, activation scales in chunks, bf16 output.
+GEMM_KERNEL = "gemm_tile_kernel<256,256,128,64,2,8,2,true,false,false>"
+GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_03_amd", "csrc", "gemm.hip")
+# HBM traffic of one prefill GEMM launch from the rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs (scaled by the 1 GiB copy calibration; see profiles/), valid
+# only for the gemm.hip source whose SHA-256 is recorded with it.
+GEMM_TRAFFIC = {"source_sha256": None, "fetch_bytes": None, "write_bytes": None}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -331,6 +340,12 @@ def main():
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6
+    traffic = None
+    if GEMM_TRAFFIC["source_sha256"] is not None:
+        import hashlib
+        with open(GEMM_SOURCE, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == GEMM_TRAFFIC["source_sha256"]:
+                traffic = GEMM_TRAFFIC["fetch_bytes"] + GEMM_TRAFFIC["write_bytes"]
     result = {
         "metric": "FP8 block-scaled GEMM TFLOP/s @M=4096,K=7168,N=18432; GB/s @M=32 decode",
         "value": round(value, 2),
@@ -349,7 +364,7 @@ def main():
                    "M": M, "N": N, "K": K, "block": 128, "scale_fmt": "fp32"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_tile_kernel<256,128,128,64,3,bf16>",
+                     "traffic": traffic, "kernel": GEMM_KERNEL,
                      "us_per_launch": round(gm_us, 3)},
     }
     if "decode_gemm_32x18432x7168" in rows:

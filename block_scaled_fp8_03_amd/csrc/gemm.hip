@@ -18,6 +18,7 @@
 // the same choice, so lane group g carries K bytes [32g, 32g + 32).  The
 // result lane l, register r is D[4 (l / 16) + r][l % 16].
 #include <algorithm>
+#include <cstdint>
 
 #include "device_common.h"
 #include "launch.h"
@@ -107,6 +108,7 @@ struct GemmParams {
   int E;                  // MoE experts
   int num_m;              // dense: m tiles; MoE: upper bound on (expert, m-tile) pairs
   int num_n;              // n tiles
+  int moe_lo, moe_hi;     // MoE: this launch takes the experts with moe_lo < rows <= moe_hi
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
@@ -221,7 +223,8 @@ gemm_tile_kernel(GemmParams p) {
             int lo = p.offsets[ee], hi = p.offsets[ee + 1];
             lo = min(max(lo, 0), p.rows);
             hi = min(max(hi, lo), p.rows);
-            cnt = (hi - lo + BM - 1) / BM;
+            const int n_rows = hi - lo;
+            cnt = (n_rows > p.moe_lo && n_rows <= p.moe_hi) ? (n_rows + BM - 1) / BM : 0;
           }
           // inclusive prefix sum over the wave
           int incl = cnt;
@@ -672,9 +675,36 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   GemmParams p{};
   p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
   p.offsets = offsets; p.rows = (int)R; p.N = (int)N; p.K = (int)K; p.E = (int)E;
+  // Experts are split by their row count.  Experts with more than
+  // kMoeSplit rows are dense GEMMs in their own right and run on the
+  // 256 x 256 tile of the dense path; the rest -- most experts under skewed
+  // routing, and most of the weight bytes -- stream their weights through
+  // 64-row tiles with three LDS stages.  Each launch finds its experts from
+  // the device offsets; the grids are upper bounds on its tile count
+  // (tiles past the end exit at once).
+#ifndef FP8BS_MOE_SPLIT
+#define FP8BS_MOE_SPLIT 64
+#endif
+  constexpr int kMoeSplit = FP8BS_MOE_SPLIT;
+  {
+    constexpr int BM = 256, BN = 256;
+    GemmParams q = p;
+    q.moe_lo = kMoeSplit;
+    q.moe_hi = INT32_MAX;
+    // sum over experts with > kMoeSplit rows of ceil(rows / BM)
+    //   <= R / BM + (number of such experts) <= R / BM + R / (kMoeSplit + 1)
+    q.num_m = (int)(R / BM + std::min<int64_t>(E, R / (kMoeSplit + 1)));
+    q.num_n = (int)((N + BN - 1) / BN);
+    if (q.num_m > 0) {
+      const hipError_t err = run_tile<BM, BN, 128, 64, 2, 8, 2, true>(q, out_f32, q.num_m * q.num_n, stream);
+      if (err != hipSuccess) return err;
+    }
+  }
   constexpr int BM = 64, BN = 256;
-  // sum_e ceil(rows_e / BM) <= R / BM + E
-  p.num_m = (int)(R / BM + E);
+  p.moe_lo = 0;
+  p.moe_hi = kMoeSplit;
+  // sum over experts with <= kMoeSplit rows of ceil(rows / BM) <= E * ceil(kMoeSplit / BM)
+  p.num_m = (int)(E * ((kMoeSplit + BM - 1) / BM));
   p.num_n = (int)((N + BN - 1) / BN);
   return run_tile<BM, BN, 64, 64, 3, 4, 2, true>(p, out_f32, p.num_m * p.num_n, stream);
 }
