@@ -11,7 +11,10 @@ prefill down-projection and the grouped MoE GEMMs -- are timed as secondary
 rows in the same run.
 
 Inputs are seeded synthetic tensors (block_scaled_fp8_03_amd.inputs), drawn on
-the device and resident in HBM before timing.  Kernel durations come from HIP
+the device and resident in HBM before timing.  Warmup runs at least W steps and
+at least WARMUP_MIN_S seconds: under sustained MFMA load the clocks take tens of
+milliseconds to settle (a GEMM's duration drifts by ~25% over its first
+~30 ms), and the timed region is meant to see the steady state.  Kernel durations come from HIP
 events recorded on the stream the kernels run on; HBM-bound rows cycle through
 enough copies of their inputs that the 256 MB Infinity Cache cannot hold them.
 The CPU baseline is the oracle (binary64 C + OpenMP) on a bounded sample of
@@ -49,7 +52,8 @@ GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_03_amd", "csrc", "gemm.hip")
 # HBM traffic of one prefill GEMM launch from the rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (scaled by the 1 GiB copy calibration; see profiles/), valid
 # only for the gemm.hip source whose SHA-256 is recorded with it.
-GEMM_TRAFFIC = {"source_sha256": None, "fetch_bytes": None, "write_bytes": None}
+GEMM_TRAFFIC = {"source_sha256": "419dad2b4252abe030dc7360833d2ddccdf5afff87b6913e19a770a6148a3b81",
+                "fetch_bytes": 837216004, "write_bytes": 152442368}
 
 
 def log(*a):
@@ -77,13 +81,26 @@ def moe_bytes(R, N, K, active_experts, out_bytes=2):
 
 # ------------------------------------------------------------------ timing
 
+WARMUP_MIN_S = 0.25
+
+
+def warm(launch, copies, warmup):
+    """At least `warmup` calls and at least WARMUP_MIN_S seconds of them."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
+        launch(i % copies)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def timed(launch, copies, steps, warmup):
     """Average duration (us) of `launch(i)`: one event pair brackets the whole
     timed region of back-to-back launches on the launch stream, so per-launch
     event overhead does not inflate short kernels."""
-    for i in range(warmup):
-        launch(i % copies)
-    torch.cuda.synchronize()
+    warm(launch, copies, warmup)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
@@ -134,12 +151,10 @@ def bench_linear_step(M, N, K, cfg, steps, warmup, dev, fmt="fp32"):
     xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-    def step():
+    def step(_=0):
         fp8bs.fp8bs_act_quant(x, xq, xs, fmt)
         fp8bs.fp8bs_gemm(xq, xs, q, s, y)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, 1, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
