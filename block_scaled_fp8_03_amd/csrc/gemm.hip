@@ -161,8 +161,10 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
 // every wave once the barrier before that issue has passed (ASC >= ST - 1).
 // Stages that start no chunk issue an out-of-range dummy load (no memory
 // traffic) when ST > 2 so that every stage has the same number of DMA ops.
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool MOE>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+// OCC workgroups share a CU (register budget set for OCC * NW / 4 waves per SIMD).
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool MOE,
+          int OCC>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))
 gemm_tile_kernel(GemmParams p) {
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static_assert(WAVES_M * WAVES_N == NW && (NW == 4 || NW == 8), "4 or 8 waves per workgroup");
@@ -599,23 +601,23 @@ gemm_decode_kernel(GemmParams p, int rows) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool MOE>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool MOE, int OCC>
 void launch_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   if (out_f32)
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, MOE, OCC><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
   else
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, MOE><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, MOE, OCC><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
 }
 
 // Chunked a_s loads (16 bytes per lane) need every row of a_s to start on a
 // 16-byte boundary.
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE, int OCC = 1>
 hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   const bool chunked = (p.K / 128) % 4 == 0 && ((uintptr_t)p.a_s & 15) == 0;
   if (chunked)
-    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, MOE>(p, out_f32, grid, stream);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, MOE, OCC>(p, out_f32, grid, stream);
   else
-    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, MOE>(p, out_f32, grid, stream);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, MOE, OCC>(p, out_f32, grid, stream);
   return hipGetLastError();
 }
 
@@ -663,6 +665,22 @@ hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const flo
 #endif
   constexpr int cfg[7] = {FP8BS_TILE_CFG};
   constexpr int BM = cfg[0], BN = cfg[1];
+  // Smaller GEMMs whose 256 x 256 tiles cannot fill the CUs run on 128 x 128
+  // tiles when those give at least one tile per two CUs, else on 64 x 64
+  // tiles with two workgroups per CU (measured: 1024 x 1536 x 7168 104 ->
+  // 30 us; 1024 x 3072 x 7168 104 -> 47 us).
+  const int cus = device_cus();
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(BM, BN) < cus) {
+    if (tiles(128, 128) >= cus / 2) {
+      p.num_m = (int)((M + 127) / 128);
+      p.num_n = (int)((N + 127) / 128);
+      return run_tile<128, 128, 64, 64, 3, 4, 2, false>(p, out_f32, p.num_m * p.num_n, stream);
+    }
+    p.num_m = (int)((M + 63) / 64);
+    p.num_n = (int)((N + 63) / 64);
+    return run_tile<64, 64, 32, 32, 3, 4, 2, false, 2>(p, out_f32, p.num_m * p.num_n, stream);
+  }
   p.num_m = (int)((M + BM - 1) / BM);
   p.num_n = (int)((N + BN - 1) / BN);
   return run_tile<FP8BS_TILE_CFG, false>(p, out_f32, p.num_m * p.num_n, stream);

@@ -45,6 +45,21 @@ SMALL = [(16, 256, 256), (1, 1, 128), (5, 7, 128), (33, 130, 256), (64, 64, 128)
          (257, 300, 1536), (520, 260, 3072)]
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (1000, 2100, 1536),   # 128 x 128 tiles, a_s in chunks
+    (1000, 2100, 640),    # 128 x 128 tiles, per-stage a_s (K/128 = 5)
+    (2050, 8200, 384),    # 256 x 256 tiles, per-stage a_s, ragged M and N
+    (2050, 8200, 1024),   # 256 x 256 tiles, a_s in chunks, ragged M and N
+])
+def test_gemm_tile_configs(M, N, K):
+    """Shapes that select each tile size of the dense path (the 64 x 64 one is
+    taken by the small shapes above), with ragged edges, compared in full."""
+    a, a_s, b, b_s = rand_operands(M, N, K, 5000 + M + N + K)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    assert_close(run_gemm(a, a_s, b, b_s, torch.float32), ref, f"gemm[{M}x{N}x{K}] f32")
+    assert_close(run_gemm(a, a_s, b, b_s, torch.bfloat16), ref, f"gemm[{M}x{N}x{K}] bf16")
+
+
 def test_gemm_unaligned_scales():
     """a_s starting 4 bytes past a 16-byte boundary: the kernel must then
     read the activation scales one float at a time (K/128 is a multiple of 4
