@@ -91,6 +91,15 @@ def zipf_topk_routing(tokens: int, experts: int, topk: int, s: float, seed: int)
             "counts": counts}
 
 
+def routing_weights(tokens: int, topk: int, seed: int) -> np.ndarray:
+    """Synthetic routing weights float32 [tokens, topk]: uniform(0.05, 1)
+    draws normalised to sum 1 per token (a stand-in for the gate's normalised
+    scores, which the expert combine multiplies each expert output by)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = rng.uniform(0.05, 1.0, (tokens, topk))
+    return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 # Workload shapes (rows of the hot-path scope table).  M, N, K follow
 # nn.Linear: x [M, K], W [N, K] (out x in).
 CONFIGS = {

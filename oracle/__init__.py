@@ -71,6 +71,10 @@ def _load():
     lib.orc_gemm_points.argtypes = [P, P, P, P, I64, P, P, I64, P]
     lib.orc_moe_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     lib.orc_moe_gemm_points.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, I64, P]
+    lib.orc_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P]
+    lib.orc_moe_route.restype = I64
+    lib.orc_moe_quant_scatter.argtypes = [P, I64, I64, ctypes.c_int, P, I64, I64, P, P]
+    lib.orc_moe_combine.argtypes = [P, P, P, I64, I64, I64, I64, P]
     lib.orc_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -238,3 +242,57 @@ def moe_gemm_points(a, a_s, b, b_s, offsets, rows, cols) -> np.ndarray:
     _load().orc_moe_gemm_points(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(offsets), E, N, K,
                                 _ptr(rows), _ptr(cols), rows.size, _ptr(out))
     return out
+
+
+# --------------------------------------------------------------- MoE dispatch
+
+def moe_route(indices: np.ndarray, E: int):
+    """Stable counting sort of routed expert ids ``int32 [T, topk]`` by expert
+    (Admin guide 6.4 / 8.4: bincount of the ids, then each expert's (token,
+    slot) pairs in token order).  Returns dict with offsets int32 [E+1],
+    row_token / row_slot int32 [R] and row_of int32 [T, topk] (-1 for ids
+    outside [0, E))."""
+    idx = _c(np.asarray(indices, dtype=np.int32), np.int32)
+    if idx.ndim != 2:
+        raise ValueError("indices must be [T, topk]")
+    T, topk = idx.shape
+    off = np.empty(E + 1, dtype=np.int32)
+    row_token = np.empty(T * topk, dtype=np.int32)
+    row_slot = np.empty(T * topk, dtype=np.int32)
+    row_of = np.empty((T, topk), dtype=np.int32)
+    R = _load().orc_moe_route(_ptr(idx), T, topk, E, _ptr(off), _ptr(row_token), _ptr(row_slot),
+                              _ptr(row_of))
+    return {"offsets": off, "row_token": row_token[:R].copy(), "row_slot": row_slot[:R].copy(),
+            "row_of": row_of}
+
+
+def moe_quant_scatter(x_bf16_bits: np.ndarray, row_of: np.ndarray, R: int, fmt: int = FMT_FP32):
+    """act_quant of each token row of x ``uint16 [T, K]`` placed at the rows
+    ``row_of [T, topk]`` names (rows no pair maps to are left zero).
+    Returns (q uint8 [R, K], s float32 [R, K/128])."""
+    x = _c(x_bf16_bits, np.uint16)
+    row_of = _c(np.asarray(row_of, dtype=np.int32), np.int32)
+    T, K = x.shape
+    if K % BLOCK or row_of.shape[0] != T:
+        raise ValueError("x must be [T, K] with K % 128 == 0 and row_of [T, topk]")
+    q = np.zeros((R, K), dtype=np.uint8)
+    s = np.zeros((R, K // BLOCK), dtype=np.float32)
+    _load().orc_moe_quant_scatter(_ptr(x), T, K, int(fmt), _ptr(row_of), row_of.shape[1], R,
+                                  _ptr(q), _ptr(s))
+    return q, s
+
+
+def moe_combine(out_bf16_bits: np.ndarray, weights: np.ndarray, row_of: np.ndarray) -> np.ndarray:
+    """y[t] = sum_k weights[t, k] * out[row_of[t, k]] in binary64, with out the
+    expert outputs as bf16 bit patterns ``uint16 [R, N]`` and weights float32
+    [T, topk].  Returns float64 [T, N]."""
+    out = _c(out_bf16_bits, np.uint16)
+    w = _c(np.asarray(weights, dtype=np.float32), np.float32)
+    row_of = _c(np.asarray(row_of, dtype=np.int32), np.int32)
+    R, N = out.shape
+    T, topk = w.shape
+    if row_of.shape != (T, topk):
+        raise ValueError("row_of must have the shape of weights")
+    y = np.empty((T, N), dtype=np.float64)
+    _load().orc_moe_combine(_ptr(out), _ptr(w), _ptr(row_of), T, topk, R, N, _ptr(y))
+    return y

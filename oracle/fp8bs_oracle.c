@@ -11,7 +11,8 @@
  *   - "DeepSeek-V3 Administrator & Developer Guide", section 8.5.1
  *     (act_quant_kernel), 8.5.2 (weight_dequant_kernel), 8.5.3
  *     (fp8_gemm_kernel), 6.3 (the FP8 path: weight scale shape
- *     ceil(out/128) x ceil(in/128)), 6.4 (MoE expert loop).
+ *     ceil(out/128) x ceil(in/128)), 6.4 and 8.4 (MoE expert loop, and the
+ *     dispatch and combine around it).
  *   - "DeepSeek-V3 User Guide", section 7 FAQ (scale_fmt ue8m0: the scale is
  *     rounded up to a power of two) and section 6 (K must be a multiple of
  *     the 128 block size).
@@ -35,6 +36,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -318,6 +320,88 @@ void orc_moe_gemm_points(const uint8_t* a, const float* a_s, const uint8_t* b, c
         while (e + 1 < E && off[e + 1] <= rows[i]) ++e;   /* expert owning the row */
         out[i] = gemm_point(a, a_s, b + e * N * K, b_s + e * nbn * nbk, K, rows[i], cols[i], dec);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MoE dispatch and combine around the expert GEMMs (Admin guide 6.4 and     */
+/* 8.4: per-expert hit counts by bincount; for each expert with hits, the     */
+/* (token, slot) pairs whose routed expert it is, in token order as          */
+/* torch.where yields them; the expert runs on those tokens' rows; its output */
+/* is scaled by the routing weight of that (token, slot) and summed into the */
+/* token's output, which starts at zero).                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Stable counting sort of the routed expert ids idx [T, topk] by expert.
+ * Expert e owns rows [off[e], off[e+1]); within it, rows follow (token,
+ * slot) order.  row_token/row_slot [R] give each row's source pair and
+ * row_of [T, topk] the row of each pair.  Ids outside [0, E) are not routed:
+ * their row_of is -1 and they take no row.  Returns R = off[E]. */
+int64_t orc_moe_route(const int32_t* idx, int64_t T, int64_t topk, int64_t E, int32_t* off,
+                      int32_t* row_token, int32_t* row_slot, int32_t* row_of) {
+    /* pass 1: hit counts per expert */
+    for (int64_t e = 0; e <= E; ++e) off[e] = 0;
+    for (int64_t i = 0; i < T * topk; ++i)
+        if (idx[i] >= 0 && idx[i] < E) off[idx[i] + 1] += 1;
+    /* exclusive prefix: first row of each expert */
+    for (int64_t e = 0; e < E; ++e) off[e + 1] += off[e];
+    /* pass 2: place every pair at its expert's next free row, in (t, s) order */
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int64_t e = 0; e < E; ++e) next[e] = off[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t k = 0; k < topk; ++k) {
+            int32_t e = idx[t * topk + k];
+            if (e < 0 || e >= E) {
+                row_of[t * topk + k] = -1;
+                continue;
+            }
+            int32_t r = next[e]++;
+            row_token[r] = (int32_t)t;
+            row_slot[r] = (int32_t)k;
+            row_of[t * topk + k] = r;
+        }
+    free(next);
+    return off[E];
+}
+
+/* The expert inputs: act_quant of every token row of x [T, K], placed at the
+ * rows its (token, slot) pairs were routed to.  The quantisation is row-local,
+ * so this is the quantisation of the gathered rows x[row_token[r]]. */
+void orc_moe_quant_scatter(const uint16_t* x, int64_t T, int64_t K, int fmt, const int32_t* row_of,
+                           int64_t topk, int64_t R, uint8_t* q, float* s) {
+    int64_t nb = K / ORC_BLOCK;
+    uint8_t* qt = (uint8_t*)malloc((size_t)K);
+    float* st = (float*)malloc(sizeof(float) * (size_t)nb);
+    for (int64_t t = 0; t < T; ++t) {
+        orc_act_quant(x + t * K, 1, K, fmt, qt, st);
+        for (int64_t k = 0; k < topk; ++k) {
+            int32_t r = row_of[t * topk + k];
+            if (r < 0 || r >= R) continue;
+            memcpy(q + (int64_t)r * K, qt, (size_t)K);
+            memcpy(s + (int64_t)r * nb, st, sizeof(float) * (size_t)nb);
+        }
+    }
+    free(qt);
+    free(st);
+}
+
+/* The combine: y[t, n] = sum over slots k of w[t, k] * out[row_of[t, k], n],
+ * with out given as bf16 bit patterns [R, N] and w as binary32.  Each term
+ * is exact in binary64 (8 + 24 significant bits); the sum of at most topk
+ * terms is formed in binary64 in slot order.  Pairs that were not routed
+ * (row_of < 0) contribute nothing. */
+void orc_moe_combine(const uint16_t* out, const float* w, const int32_t* row_of, int64_t T,
+                     int64_t topk, int64_t R, int64_t N, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < topk; ++k) {
+                int32_t r = row_of[t * topk + k];
+                if (r < 0 || r >= R) continue;
+                acc += (double)w[t * topk + k] * (double)orc_bf16_to_f32(out[(int64_t)r * N + n]);
+            }
+            y[t * N + n] = acc;
+        }
 }
 
 int orc_num_threads(void) {

@@ -434,3 +434,117 @@ def test_routing_invariants():
         assert np.all(np.diff(toks) > 0)
         assert set(toks) == set(np.nonzero((ch == e).any(1))[0])
     assert r["counts"].argmax() == 0
+
+
+# ---------------------------------------------------- MoE dispatch and combine
+
+def _where_loop_rows(indices, E):
+    """The pages' expert loop (Admin guide 6.4): for each expert, the (token,
+    slot) pairs routed to it, in the order torch.where yields them."""
+    rows = []
+    for e in range(E):
+        tok, slot = np.nonzero(indices == e)
+        rows += list(zip(tok.tolist(), slot.tolist()))
+    return rows
+
+
+@pytest.mark.parametrize("T,topk,E,seed", [(1, 1, 1, 0), (7, 3, 5, 1), (64, 8, 16, 2), (300, 8, 64, 3)])
+def test_moe_route_matches_where_loop(orc, T, topk, E, seed):
+    """The counting sort against the per-expert torch.where formulation (a
+    different algorithm): same rows in the same order, offsets = bincount
+    prefix sums, row_of the inverse map.  Ids may repeat within a token."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, (T, topk)).astype(np.int32)
+    r = orc.moe_route(idx, E)
+    rows = _where_loop_rows(idx, E)
+    assert list(zip(r["row_token"].tolist(), r["row_slot"].tolist())) == rows
+    assert np.array_equal(np.diff(r["offsets"]), np.bincount(idx.ravel(), minlength=E))
+    assert r["offsets"][0] == 0 and r["offsets"][-1] == T * topk
+    for i, (t, k) in enumerate(rows):
+        assert r["row_of"][t, k] == i
+
+
+def test_moe_route_distinct_experts_zipf(orc):
+    """The C4-style routing (distinct experts per token, Zipf-skewed): the
+    sort reproduces the harness's own grouping by (expert, token)."""
+    g = inputs.zipf_topk_routing(512, 64, 8, 1.1, 7)
+    r = orc.moe_route(g["choice"].astype(np.int32), 64)
+    assert np.array_equal(r["offsets"], g["offsets"])
+    assert np.array_equal(r["row_token"], g["token"])
+
+
+def test_moe_route_invalid_ids(orc):
+    """Ids outside [0, E) take no row and map to -1; empty experts get an
+    empty range; T = 0 gives R = 0."""
+    idx = np.array([[0, -1, 3], [5, 3, 3], [2, 7, 0]], dtype=np.int32)
+    r = orc.moe_route(idx, 5)
+    assert list(r["offsets"]) == [0, 2, 2, 3, 6, 6]
+    assert r["row_of"][0, 1] == -1 and r["row_of"][1, 0] == -1 and r["row_of"][2, 1] == -1
+    assert sorted(r["row_of"][r["row_of"] >= 0].tolist()) == list(range(6))
+    r0 = orc.moe_route(np.zeros((0, 8), dtype=np.int32), 4)
+    assert list(r0["offsets"]) == [0] * 5 and r0["row_token"].size == 0
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_moe_quant_scatter_is_gather_then_quant(orc, fmt):
+    """Quantise-then-scatter equals gather-then-quantise (act_quant is row
+    local): every routed row holds act_quant of its token's row."""
+    rng = np.random.default_rng(20 + fmt)
+    T, topk, E, K = 37, 4, 9, 384
+    idx = rng.integers(0, E, (T, topk)).astype(np.int32)
+    r = orc.moe_route(idx, E)
+    R = int(r["offsets"][-1])
+    x = inputs.bf16_bits(inputs.normal_bf16((T, K), 1.0, 99, outlier_frac=0.02, outlier_mult=50.0))
+    q, s = orc.moe_quant_scatter(x, r["row_of"], R, fmt)
+    qg, sg = orc.act_quant(x[r["row_token"]], fmt)
+    assert np.array_equal(q, qg) and np.array_equal(s.view(np.uint32), sg.view(np.uint32))
+
+
+def test_moe_combine_matches_expert_loop(orc):
+    """The token-major combine against the pages' expert-major loop
+    y[idx] += expert(x[idx]) * weights[idx, top] (Admin guide 6.4), both in
+    float64, where expert e is a fixed random linear map: the combine reads
+    the expert outputs laid out in routed-row order."""
+    rng = np.random.default_rng(31)
+    T, topk, E, D, N = 50, 4, 7, 16, 24
+    idx = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, topk)).astype(np.float32)
+    x = rng.standard_normal((T, D))
+    W = rng.standard_normal((E, D, N))
+    r = orc.moe_route(idx, E)
+    R = int(r["offsets"][-1])
+    experts = np.repeat(np.arange(E), np.diff(r["offsets"]))
+    out = np.stack([x[r["row_token"][i]] @ W[experts[i]] for i in range(R)])
+    out_bits = inputs.bf16_bits(torch.from_numpy(out).float().to(torch.bfloat16))
+    out_bf = torch.from_numpy(out_bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    y = orc.moe_combine(out_bits, w, r["row_of"])
+    ref = np.zeros((T, N))
+    for e in range(E):
+        tok, top = np.nonzero(idx == e)
+        rows = r["row_of"][tok, top]
+        ref[tok] += out_bf[rows] * w[tok, top][:, None].astype(np.float64)
+    assert np.allclose(y, ref, rtol=1e-14, atol=1e-14)
+
+
+def test_moe_combine_one_hot_and_linear(orc):
+    """One-hot weights copy the selected row exactly; scaling all weights by
+    a power of two scales y exactly; unrouted pairs contribute nothing."""
+    rng = np.random.default_rng(41)
+    T, topk, E, N = 20, 3, 6, 40
+    idx = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    r = orc.moe_route(idx, E)
+    R = int(r["offsets"][-1])
+    out = inputs.bf16_bits(torch.randn(R, N, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16))
+    out_f = torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).double().numpy()
+    pick = rng.integers(0, topk, T)
+    w = np.zeros((T, topk), dtype=np.float32)
+    w[np.arange(T), pick] = 1.0
+    y = orc.moe_combine(out, w, r["row_of"])
+    assert np.array_equal(y, out_f[r["row_of"][np.arange(T), pick]])
+    w2 = rng.uniform(0.1, 1, (T, topk)).astype(np.float32)
+    assert np.array_equal(orc.moe_combine(out, w2 * 4, r["row_of"]), 4 * orc.moe_combine(out, w2, r["row_of"]))
+    row_of = r["row_of"].copy()
+    row_of[:, 0] = -1
+    w3 = w2.copy()
+    w3[:, 0] = 0
+    assert np.array_equal(orc.moe_combine(out, w2, row_of), orc.moe_combine(out, w3, r["row_of"]))
