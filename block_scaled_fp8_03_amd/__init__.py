@@ -6,8 +6,11 @@ library's HIP kernels.  PyTorch provides device memory and streams.
 
 Raw entry points carry the C names and take caller-allocated outputs:
 ``fp8bs_act_quant``, ``fp8bs_weight_quant``, ``fp8bs_weight_dequant``,
-``fp8bs_gemm``, ``fp8bs_moe_gemm``.  Allocating conveniences: ``act_quant``,
-``weight_quant``, ``weight_dequant``, ``fp8_gemm``, ``moe_gemm``, ``linear``.
+``fp8bs_gemm``, ``fp8bs_moe_gemm`` and the MoE dispatch/combine steps
+``fp8bs_moe_route``, ``fp8bs_moe_quant_scatter``, ``fp8bs_moe_combine``.
+Allocating conveniences: ``act_quant``, ``weight_quant``, ``weight_dequant``,
+``fp8_gemm``, ``moe_gemm``, ``linear``, ``moe_route``, ``moe_quant_scatter``,
+``moe_combine``.
 
 The operations follow the DeepSeek-V3 inference pages ("DeepSeek-V3
 Administrator & Developer Guide", sections 6.3, 6.4, 8.5.1-8.5.3; "DeepSeek-V3
@@ -24,8 +27,9 @@ import torch
 __all__ = [
     "SCALE_FP32", "SCALE_UE8M0", "OUT_BF16", "OUT_F32", "Fp8bsError", "library_path", "lib",
     "fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
-    "fp8bs_moe_gemm", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm",
-    "linear",
+    "fp8bs_moe_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter", "fp8bs_moe_combine",
+    "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm", "linear", "moe_route",
+    "moe_quant_scatter", "moe_combine",
 ]
 
 SCALE_FP32 = 0
@@ -65,8 +69,13 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_weight_dequant.argtypes = [P, P, P, I64, I64, P]
     L.fp8bs_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     L.fp8bs_moe_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, P]
+    L.fp8bs_moe_route_workspace_size.argtypes = [I64, I64, I64]
+    L.fp8bs_moe_route_workspace_size.restype = I64
+    L.fp8bs_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
+    L.fp8bs_moe_quant_scatter.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
+    L.fp8bs_moe_combine.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     for fn in ("fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
-               "fp8bs_moe_gemm"):
+               "fp8bs_moe_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter", "fp8bs_moe_combine"):
         getattr(L, fn).restype = I
     _lib = L
     return L
@@ -177,6 +186,52 @@ def fp8bs_moe_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: tor
           _need(c, (torch.bfloat16, torch.float32), "c"), R, E, N, K, _out_code(c), _stream(a))
 
 
+def fp8bs_moe_route(indices: torch.Tensor, E: int, offsets: torch.Tensor, row_token: torch.Tensor,
+                    row_of: torch.Tensor, workspace: torch.Tensor) -> None:
+    """Stable counting sort of routed expert ids int32 [T, topk] by expert:
+    offsets [E+1], row_token [T*topk], row_of [T, topk] (see fp8bs.h)."""
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, topk]")
+    T, topk = indices.shape
+    need = lib().fp8bs_moe_route_workspace_size(T, topk, E)
+    if need < 0:
+        raise ValueError("sizes out of range")
+    if (tuple(offsets.shape) != (E + 1,) or tuple(row_token.shape) != (T * topk,)
+            or tuple(row_of.shape) != (T, topk)):
+        raise ValueError("offsets must be [E+1], row_token [T*topk] and row_of [T, topk]")
+    nbytes = workspace.numel() * workspace.element_size()
+    ws = _need(workspace, (torch.uint8, torch.int32), "workspace") if nbytes else None
+    _call("fp8bs_moe_route", _need(indices, (torch.int32,), "indices"), T, topk, E,
+          _need(offsets, (torch.int32,), "offsets"), _need(row_token, (torch.int32,), "row_token"),
+          _need(row_of, (torch.int32,), "row_of"), ws, nbytes, _stream(indices))
+
+
+def fp8bs_moe_quant_scatter(x: torch.Tensor, row_of: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
+                            scale_fmt=SCALE_FP32) -> None:
+    """act_quant of each token row of x bf16 [T, K] written to its routed rows
+    of q e4m3 [R, K] and s float32 [R, K/128]."""
+    T, K = x.shape
+    R = q.shape[0]
+    if row_of.dim() != 2 or row_of.shape[0] != T:
+        raise ValueError("row_of must be [T, topk]")
+    if tuple(q.shape) != (R, K) or K % BLOCK or tuple(s.shape) != (R, K // BLOCK):
+        raise ValueError("q must be [R, K] and s [R, K/128], K a multiple of 128")
+    _call("fp8bs_moe_quant_scatter", _need(x, (torch.bfloat16,), "x"),
+          _need(row_of, (torch.int32,), "row_of"), _need(q, _F8, "q"),
+          _need(s, (torch.float32,), "s"), T, row_of.shape[1], R, K, _fmt(scale_fmt), _stream(x))
+
+
+def fp8bs_moe_combine(out: torch.Tensor, w: torch.Tensor, row_of: torch.Tensor, y: torch.Tensor) -> None:
+    """y [T, N] = sum_k w[t, k] * out[row_of[t, k]] (out bf16 [R, N], y bf16 or float32)."""
+    R, N = out.shape
+    T, topk = w.shape
+    if tuple(row_of.shape) != (T, topk) or tuple(y.shape) != (T, N):
+        raise ValueError("row_of must be [T, topk] like w, and y [T, N]")
+    _call("fp8bs_moe_combine", _need(out, (torch.bfloat16,), "out"), _need(w, (torch.float32,), "w"),
+          _need(row_of, (torch.int32,), "row_of"), _need(y, (torch.bfloat16, torch.float32), "y"),
+          T, topk, R, N, _out_code(y), _stream(out))
+
+
 # ------------------------------------------------------ allocating wrappers
 
 def act_quant(x: torch.Tensor, scale_fmt="fp32"):
@@ -223,3 +278,35 @@ def linear(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, scale_fmt="fp32"
     q, s = act_quant(x.reshape(-1, K), scale_fmt)
     y = fp8_gemm(q, s, w, w_s, out_dtype)
     return y.view(*x.shape[:-1], w.shape[0])
+
+
+def moe_route(indices: torch.Tensor, E: int):
+    """Routed expert ids int32 [T, topk] -> (offsets [E+1], row_token [T*topk],
+    row_of [T, topk]), all int32 on the device; no host synchronisation."""
+    T, topk = indices.shape
+    dev = indices.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    need = lib().fp8bs_moe_route_workspace_size(T, topk, E)
+    if need < 0:
+        raise ValueError("sizes out of range")
+    ws = torch.empty(max(need, 0), dtype=torch.uint8, device=dev)
+    fp8bs_moe_route(indices, E, offsets, row_token, row_of, ws)
+    return offsets, row_token, row_of
+
+
+def moe_quant_scatter(x: torch.Tensor, row_of: torch.Tensor, R: int, scale_fmt="fp32"):
+    """The expert inputs: (q e4m3 [R, K], s float32 [R, K/128])."""
+    K = x.shape[-1]
+    q = torch.empty((R, K), dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((R, K // BLOCK), dtype=torch.float32, device=x.device)
+    fp8bs_moe_quant_scatter(x, row_of, q, s, scale_fmt)
+    return q, s
+
+
+def moe_combine(out: torch.Tensor, w: torch.Tensor, row_of: torch.Tensor,
+                out_dtype=torch.bfloat16) -> torch.Tensor:
+    y = torch.empty((w.shape[0], out.shape[1]), dtype=out_dtype, device=out.device)
+    fp8bs_moe_combine(out, w, row_of, y)
+    return y

@@ -149,4 +149,76 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
                                           out_dtype == FP8BS_OUT_F32, (hipStream_t)stream));
 }
 
+int64_t fp8bs_moe_route_workspace_size(int64_t T, int64_t topk, int64_t E) {
+  if (T < 0 || topk < 1 || E < 1 || E > kLimitInt) return -1;
+  const int64_t P = mul(T, topk);
+  if (P < 0 || P > kLimitInt) return -1;
+  const int64_t bytes = mul(mul(cdiv(P, 512), E), 4);
+  return bytes < 0 ? -1 : bytes;
+}
+
+int fp8bs_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E, int32_t* offsets,
+                    int32_t* row_token, int32_t* row_of, void* workspace,
+                    int64_t workspace_bytes, void* stream) {
+  const int64_t need = fp8bs_moe_route_workspace_size(T, topk, E);
+  if (need < 0) return FP8BS_ERR_SHAPE;
+  if (workspace_bytes < need) return FP8BS_ERR_SHAPE;
+  const int64_t P = T * topk;
+  if (!offsets) return FP8BS_ERR_NULL;
+  if (P > 0 && (!indices || !row_token || !row_of || !workspace)) return FP8BS_ERR_NULL;
+  if (!aligned(indices, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) ||
+      !aligned(row_of, 4) || !aligned(workspace, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t ob = 4 * (E + 1), pb = 4 * P;
+  if (overlap(offsets, ob, indices, pb) || overlap(row_token, pb, indices, pb) ||
+      overlap(row_of, pb, indices, pb) || overlap(offsets, ob, row_token, pb) ||
+      overlap(offsets, ob, row_of, pb) || overlap(row_token, pb, row_of, pb) ||
+      overlap(workspace, need, indices, pb) || overlap(workspace, need, offsets, ob) ||
+      overlap(workspace, need, row_token, pb) || overlap(workspace, need, row_of, pb))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_moe_route(indices, T, topk, E, offsets, row_token, row_of,
+                                           workspace, (hipStream_t)stream));
+}
+
+int fp8bs_moe_quant_scatter(const void* x_bf16, const int32_t* row_of, void* q_e4m3, float* s,
+                            int64_t T, int64_t topk, int64_t R, int64_t K, int scale_fmt,
+                            void* stream) {
+  if (T < 0 || topk < 1 || R < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (scale_fmt != FP8BS_SCALE_FP32 && scale_fmt != FP8BS_SCALE_UE8M0) return FP8BS_ERR_ENUM;
+  const int64_t nx = mul(T, K), nq = mul(R, K), P = mul(T, topk);
+  if (nx < 0 || nq < 0 || P < 0 || P > kLimitInt || mul(nx, 2) < 0 || R > kLimitInt)
+    return FP8BS_ERR_SHAPE;
+  if (nx == 0 || nq == 0) return FP8BS_OK;
+  if (!x_bf16 || !row_of || !q_e4m3 || !s) return FP8BS_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(s, 4) || !aligned(row_of, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t ns = 4 * (nq / 128);
+  if (overlap(q_e4m3, nq, x_bf16, 2 * nx) || overlap(s, ns, x_bf16, 2 * nx) ||
+      overlap(q_e4m3, nq, s, ns) || overlap(q_e4m3, nq, row_of, 4 * P) ||
+      overlap(s, ns, row_of, 4 * P))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_moe_quant_scatter(x_bf16, row_of, q_e4m3, s, T, topk, R, K,
+                                                   scale_fmt == FP8BS_SCALE_UE8M0,
+                                                   (hipStream_t)stream));
+}
+
+int fp8bs_moe_combine(const void* out_bf16, const float* w, const int32_t* row_of, void* y,
+                      int64_t T, int64_t topk, int64_t R, int64_t N, int out_dtype, void* stream) {
+  if (T < 0 || topk < 1 || R < 0 || N < 0) return FP8BS_ERR_SHAPE;
+  if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ENUM;
+  const int64_t no = mul(R, N), ny = mul(T, N), P = mul(T, topk);
+  if (no < 0 || ny < 0 || P < 0 || P > kLimitInt || mul(no, 2) < 0 || mul(ny, 4) < 0 ||
+      R > kLimitInt)
+    return FP8BS_ERR_SHAPE;
+  if (ny == 0) return FP8BS_OK;
+  if (!w || !row_of || !y || (no > 0 && !out_bf16)) return FP8BS_ERR_NULL;
+  if (!aligned(out_bf16, 16) || !aligned(y, 16) || !aligned(w, 4) || !aligned(row_of, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t yb = ny * (out_dtype == FP8BS_OUT_F32 ? 4 : 2);
+  if (overlap(y, yb, out_bf16, 2 * no) || overlap(y, yb, w, 4 * P) || overlap(y, yb, row_of, 4 * P))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_moe_combine(out_bf16, w, row_of, y, T, topk, R, N,
+                                             out_dtype == FP8BS_OUT_F32, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -20,4 +20,15 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
                            const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N,
                            int64_t K, bool out_f32, hipStream_t stream);
 
+hipError_t launch_moe_quant_scatter(const void* x, const int32_t* row_of, void* q, float* s,
+                                    int64_t T, int64_t topk, int64_t R, int64_t K, bool ue8m0,
+                                    hipStream_t stream);
+int64_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+hipError_t launch_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E,
+                            int32_t* offsets, int32_t* row_token, int32_t* row_of, void* workspace,
+                            hipStream_t stream);
+hipError_t launch_moe_combine(const void* out, const float* w, const int32_t* row_of, void* y,
+                              int64_t T, int64_t topk, int64_t R, int64_t N, bool out_f32,
+                              hipStream_t stream);
+
 }  // namespace fp8bs

@@ -25,11 +25,18 @@ constexpr int kAqThreads = 256;
 constexpr int kAqPasses = 4;
 constexpr int kAqBlocksPerWg = (kAqThreads / 16) * kAqPasses;
 
-template <bool UE8M0>
+// SCATTER: x is the token matrix [T, K] and the codes and scale of token t's
+// block j go to every row r = row_of[t * topk + k] (k < topk, 0 <= r < R) of
+// q [R, K] / s [R, K/128] instead of to row t -- the expert inputs of the MoE
+// dispatch (quantisation is row local, so this equals quantising the
+// gathered rows).
+template <bool UE8M0, bool SCATTER>
 __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __restrict__ x,
                                                                uint2* __restrict__ q,
                                                                float* __restrict__ s,
-                                                               int64_t nblocks) {
+                                                               int64_t nblocks,
+                                                               const int32_t* __restrict__ row_of,
+                                                               int topk, int64_t nb, int64_t R) {
   const int lane16 = threadIdx.x & 15;
   const int row = threadIdx.x >> 4;
   const int64_t first = (int64_t)blockIdx.x * kAqBlocksPerWg + row;
@@ -61,8 +68,18 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
     o.y = pack4_e4m3(div_markstein(f[4], sc, r), div_markstein(f[5], sc, r),
                      div_markstein(f[6], sc, r), div_markstein(f[7], sc, r));
     if (b < nblocks) {
-      q[b * 16 + lane16] = o;
-      if (lane16 == 0) s[b] = sc;
+      if (!SCATTER) {
+        q[b * 16 + lane16] = o;
+        if (lane16 == 0) s[b] = sc;
+      } else {
+        const int64_t t = b / nb, j = b - t * nb;
+        for (int k = 0; k < topk; ++k) {
+          const int64_t r = row_of[t * topk + k];
+          if (r < 0 || r >= R) continue;
+          q[(r * nb + j) * 16 + lane16] = o;
+          if (lane16 == 0) s[r * nb + j] = sc;
+        }
+      }
     }
   }
 }
@@ -73,11 +90,27 @@ hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t
   if (nblocks == 0) return hipSuccess;
   const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
   if (ue8m0)
-    act_quant_kernel<true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
-        (const uint4*)x, (uint2*)q, s, nblocks);
+    act_quant_kernel<true, false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
+        (const uint4*)x, (uint2*)q, s, nblocks, nullptr, 0, 0, 0);
   else
-    act_quant_kernel<false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
-        (const uint4*)x, (uint2*)q, s, nblocks);
+    act_quant_kernel<false, false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
+        (const uint4*)x, (uint2*)q, s, nblocks, nullptr, 0, 0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_quant_scatter(const void* x, const int32_t* row_of, void* q, float* s,
+                                    int64_t T, int64_t topk, int64_t R, int64_t K, bool ue8m0,
+                                    hipStream_t stream) {
+  const int64_t nb = K / kBlock;
+  const int64_t nblocks = T * nb;
+  if (nblocks == 0 || R == 0) return hipSuccess;
+  const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
+  if (ue8m0)
+    act_quant_kernel<true, true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
+        (const uint4*)x, (uint2*)q, s, nblocks, row_of, (int)topk, nb, R);
+  else
+    act_quant_kernel<false, true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
+        (const uint4*)x, (uint2*)q, s, nblocks, row_of, (int)topk, nb, R);
   return hipGetLastError();
 }
 

@@ -154,6 +154,77 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
                    const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N, int64_t K,
                    int out_dtype, void* stream);
 
+/*
+ * MoE dispatch and combine -- the steps around fp8bs_moe_gemm in the expert
+ * loop of the Admin guide (6.4; the annotated forward pass in 8.4): hit
+ * counts of the routed expert ids, each expert's (token, slot) pairs in token
+ * order, the expert run on those tokens' rows, and the expert outputs scaled
+ * by the routing weight of their (token, slot) and summed per token.
+ *
+ * moe_route_workspace_size -- bytes of device workspace fp8bs_moe_route
+ * needs for T tokens, topk slots and E experts (4 * ceil(T*topk/512) * E;
+ * 0 when T*topk == 0).  Returns -1 for sizes fp8bs_moe_route rejects.
+ */
+int64_t fp8bs_moe_route_workspace_size(int64_t T, int64_t topk, int64_t E);
+
+/*
+ * moe_route -- stable counting sort of the routed expert ids by expert.
+ *
+ *   indices    in   DEVICE int32 [T, topk]: the expert of each (token, slot)
+ *   offsets    out  DEVICE int32 [E+1]: expert e owns rows [offsets[e],
+ *                   offsets[e+1]); offsets[E] = R, the number of pairs whose
+ *                   id lies in [0, E)
+ *   row_token  out  DEVICE int32 [T*topk]: the token of each row r < R, rows
+ *                   of one expert in (token, slot) order (the order the
+ *                   pages' torch.where yields); entries >= R untouched
+ *   row_of     out  DEVICE int32 [T, topk]: the row of each (token, slot), or
+ *                   -1 when its id is outside [0, E) (such a pair is not
+ *                   routed and takes no row)
+ *   workspace  tmp  DEVICE, >= fp8bs_moe_route_workspace_size bytes, 4-byte
+ *                   aligned; its contents are scratch (nothing needs clearing)
+ *   T >= 0, 1 <= topk, 1 <= E, T*topk < 2^31.  Three kernel launches; the
+ *   result does not depend on timing (no atomics).
+ */
+int fp8bs_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E, int32_t* offsets,
+                    int32_t* row_token, int32_t* row_of, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/*
+ * moe_quant_scatter -- the expert inputs: act_quant (as fp8bs_act_quant) of
+ * every token row of x, written to each row its (token, slot) pairs were
+ * routed to.  Quantisation is row local, so row r holds act_quant of
+ * x[row_token[r]].
+ *
+ *   x        in   bf16 [T, K], K % 128 == 0
+ *   row_of   in   DEVICE int32 [T, topk] (from fp8bs_moe_route); entries
+ *                 outside [0, R) are skipped
+ *   q        out  e4m3 [R, K]; s out float32 [R, K/128]; rows no pair maps
+ *                 to are left untouched
+ *   scale_fmt     FP8BS_SCALE_FP32 or FP8BS_SCALE_UE8M0
+ * Alignment as fp8bs_act_quant; row_of 4-byte aligned.  If row_of maps two
+ * pairs to one row, that row receives one of the two (identical for a
+ * token's own duplicates).
+ */
+int fp8bs_moe_quant_scatter(const void* x_bf16, const int32_t* row_of, void* q_e4m3, float* s,
+                            int64_t T, int64_t topk, int64_t R, int64_t K, int scale_fmt,
+                            void* stream);
+
+/*
+ * moe_combine -- y[t, n] = sum_k w[t, k] * out[row_of[t, k], n], summed in
+ * float32 in slot order (the pages accumulate y in place, expert by expert;
+ * here a token's at most topk terms are summed once and rounded once).
+ *
+ *   out      in   bf16 [R, N]: expert outputs in routed-row order
+ *   w        in   float32 [T, topk]: routing weights
+ *   row_of   in   DEVICE int32 [T, topk]; pairs outside [0, R) contribute 0
+ *   y        out  [T, N] bf16 or float32 (out_dtype); overwritten, not
+ *                 accumulated into
+ * out and y 16-byte aligned, w and row_of 4-byte aligned; N >= 0, T >= 0,
+ * topk >= 1, R >= 0.
+ */
+int fp8bs_moe_combine(const void* out_bf16, const float* w, const int32_t* row_of, void* y,
+                      int64_t T, int64_t topk, int64_t R, int64_t N, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -111,6 +111,40 @@ def test_moe_gemm_validation(L):
     assert m(None, None, None, None, None, None, 8, 0, 4, 128, 0, None) == OK
 
 
+def test_moe_route_validation(L):
+    r = L.fp8bs_moe_route
+    ws = L.fp8bs_moe_route_workspace_size
+    assert ws(4096, 8, 256) == 4 * 64 * 256
+    assert ws(0, 8, 256) == 0 and ws(3, 1, 5) == 4 * 1 * 5
+    assert ws(-1, 8, 4) == -1 and ws(4, 0, 4) == -1 and ws(4, 8, 0) == -1 and ws(1 << 30, 8, 4) == -1
+    need = ws(100, 8, 16)
+    assert r(P0, 100, 8, 16, P1, P2, P3, P4, need - 4, None) == SHAPE      # workspace too small
+    assert r(P0, 100, 0, 16, P1, P2, P3, P4, need, None) == SHAPE          # topk = 0
+    assert r(P0, 100, 8, 16, None, P2, P3, P4, need, None) == NULL
+    assert r(P0, 100, 8, 16, P1, P2, P3, None, need, None) == NULL
+    assert r(P0, 100, 8, 16, P1 + 2, P2, P3, P4, need, None) == ALIGN
+    assert r(P0, 100, 8, 16, P1, P2, P2 + 64, P4, need, None) == ALIAS     # row_of inside row_token
+    assert r(P0, 100, 8, 16, P1, P2, P3, P0 + 64, need, None) == ALIAS     # workspace over indices
+
+
+def test_moe_quant_scatter_and_combine_validation(L):
+    q = L.fp8bs_moe_quant_scatter
+    assert q(P0, P1, P2, P3, 4, 8, 32, 100, 0, None) == SHAPE             # K % 128
+    assert q(P0, P1, P2, P3, 4, 0, 32, 128, 0, None) == SHAPE             # topk = 0
+    assert q(P0, P1, P2, P3, 4, 8, 32, 128, 3, None) == ENUM
+    assert q(P0, None, P2, P3, 4, 8, 32, 128, 0, None) == NULL
+    assert q(P0, P1, P2 + 8, P3, 4, 8, 32, 128, 0, None) == ALIGN
+    assert q(P0, P1, P1, P3, 4, 8, 32, 128, 0, None) == ALIAS             # q over row_of
+    assert q(None, None, None, None, 0, 8, 32, 128, 0, None) == OK         # no tokens
+    c = L.fp8bs_moe_combine
+    assert c(P0, P1, P2, P3, 4, 8, 32, -1, 0, None) == SHAPE
+    assert c(P0, P1, P2, P3, 4, 8, 32, 64, 5, None) == ENUM
+    assert c(P0, None, P2, P3, 4, 8, 32, 64, 0, None) == NULL
+    assert c(P0, P1, P2, P3 + 4, 4, 8, 32, 64, 1, None) == ALIGN
+    assert c(P0, P1, P2, P0 + 128, 4, 8, 32, 64, 0, None) == ALIAS         # y inside out
+    assert c(None, None, None, None, 0, 8, 32, 64, 0, None) == OK
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.bfloat16)

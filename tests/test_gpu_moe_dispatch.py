@@ -1,0 +1,186 @@
+"""GPU parity of the MoE dispatch and combine against the CPU oracle, through
+the C ABI: the route (counting sort by expert) and the scattered act_quant are
+compared exactly (every offset, row index, e4m3 byte and scale bit); the
+combine within the rounding its float32 sum and bf16 store allow:
+|gpu - ref| <= 2^-20 * S (+ 2^-8 |ref| for the bf16 store), S = sum_k |w out|."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_03_amd as fp8bs
+import oracle
+from block_scaled_fp8_03_amd import inputs
+from gpu_util import DEV, assert_bytes_equal, f32_bits, u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+
+
+def to_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def check_route(idx: np.ndarray, E: int, what: str):
+    T, topk = idx.shape
+    off, row_token, row_of = fp8bs.moe_route(to_i32(idx), E)
+    torch.cuda.synchronize()
+    ref = oracle.moe_route(idx, E)
+    R = int(ref["offsets"][-1])
+    assert np.array_equal(off.cpu().numpy(), ref["offsets"]), what + " offsets"
+    assert np.array_equal(row_token.cpu().numpy()[:R], ref["row_token"]), what + " row_token"
+    assert np.array_equal(row_of.cpu().numpy(), ref["row_of"]), what + " row_of"
+    return ref
+
+
+@pytest.mark.parametrize("T,topk,E,seed", [
+    (1, 1, 1, 0), (5, 3, 4, 1), (100, 8, 16, 2),      # repeats within a token allowed
+    (700, 8, 300, 3),                                 # experts > threads of a workgroup
+    (2000, 2, 3000, 4),                               # experts > one scan round
+    (513, 1, 7, 5),                                   # one pair past a chunk boundary
+])
+def test_route_random(T, topk, E, seed):
+    rng = np.random.default_rng(seed)
+    check_route(rng.integers(0, E, (T, topk)).astype(np.int32), E, f"route[{T}x{topk},E={E}]")
+
+
+def test_route_invalid_ids_and_empty():
+    rng = np.random.default_rng(9)
+    idx = rng.integers(-3, 12, (300, 4)).astype(np.int32)      # ids outside [0, 10) are dropped
+    ref = check_route(idx, 10, "route invalid ids")
+    assert (ref["row_of"] < 0).sum() == ((idx < 0) | (idx >= 10)).sum()
+    off, _, _ = fp8bs.moe_route(torch.zeros((0, 8), dtype=torch.int32, device=DEV), 5)
+    torch.cuda.synchronize()
+    assert off.cpu().tolist() == [0] * 6
+
+
+def test_route_full_size_zipf():
+    """The MoE workload: 4096 tokens, top-8 of 256 experts, Zipf(1.1)."""
+    cfg = inputs.CONFIGS[4]
+    g = inputs.zipf_topk_routing(cfg["tokens"], cfg["experts"], cfg["topk"], cfg["zipf_s"],
+                                 inputs.seed_for(4, 9))
+    check_route(g["choice"].astype(np.int32), cfg["experts"], "route C4")
+
+
+def check_quant_scatter(T, topk, E, K, fmt, seed, outliers=False):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, (T, topk)).astype(np.int32)
+    ref_route = oracle.moe_route(idx, E)
+    R = int(ref_route["offsets"][-1])
+    x = inputs.normal_bf16((T, K), 1.0, seed, outlier_frac=0.01 if outliers else 0.0, outlier_mult=50.0)
+    q, s = fp8bs.moe_quant_scatter(x.to(DEV), to_i32(ref_route["row_of"]), R, fmt)
+    torch.cuda.synchronize()
+    qr, sr = oracle.moe_quant_scatter(inputs.bf16_bits(x), ref_route["row_of"], R, fmt)
+    what = f"quant_scatter[{T}x{K} topk={topk} fmt={fmt}]"
+    assert_bytes_equal(f32_bits(s), sr.view(np.uint32), what + " scales")
+    assert_bytes_equal(u8(q), qr, what + " codes")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("T,topk,E,K", [(1, 1, 1, 128), (37, 4, 9, 384), (300, 8, 64, 1024)])
+def test_quant_scatter_small(T, topk, E, K, fmt):
+    check_quant_scatter(T, topk, E, K, fmt, 40 + T + K, outliers=True)
+
+
+def test_quant_scatter_full_size():
+    """The MoE up-projection input: 4096 tokens x 7168, Zipf top-8 routing."""
+    cfg = inputs.CONFIGS[4]
+    g = inputs.zipf_topk_routing(cfg["tokens"], cfg["experts"], cfg["topk"], cfg["zipf_s"],
+                                 inputs.seed_for(4, 9))
+    ref_route = oracle.moe_route(g["choice"].astype(np.int32), cfg["experts"])
+    R = int(ref_route["offsets"][-1])
+    x = inputs.normal_bf16((cfg["tokens"], cfg["up"]["K"]), 1.0, inputs.seed_for(4, 0))
+    q, s = fp8bs.moe_quant_scatter(x.to(DEV), to_i32(ref_route["row_of"]), R, "fp32")
+    torch.cuda.synchronize()
+    qr, sr = oracle.moe_quant_scatter(inputs.bf16_bits(x), ref_route["row_of"], R, 0)
+    assert_bytes_equal(f32_bits(s), sr.view(np.uint32), "quant_scatter C4 scales")
+    assert_bytes_equal(u8(q), qr, "quant_scatter C4 codes")
+
+
+def check_combine(out_bits: np.ndarray, w: np.ndarray, row_of: np.ndarray, what: str):
+    out_dev = torch.from_numpy(out_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    w_dev = torch.from_numpy(w).to(DEV)
+    ro_dev = to_i32(row_of)
+    ref = oracle.moe_combine(out_bits, w, row_of)
+    S = oracle.moe_combine(out_bits & 0x7FFF, np.abs(w), row_of)
+    for dt in (torch.float32, torch.bfloat16):
+        y = fp8bs.moe_combine(out_dev, w_dev, ro_dev, dt)
+        torch.cuda.synchronize()
+        got = y.float().cpu().numpy().astype(np.float64)
+        bar = 2.0 ** -20 * S + (2.0 ** -8 * np.abs(ref) if dt == torch.bfloat16 else 0.0) + 1e-30
+        bad = np.abs(got - ref) > bar
+        assert not bad.any(), f"{what} {dt}: {bad.sum()} outside, first {np.argwhere(bad)[:4].tolist()}"
+
+
+@pytest.mark.parametrize("T,topk,E,N", [
+    (1, 1, 1, 8), (33, 4, 8, 64), (200, 8, 32, 520),   # vector path (N % 8 == 0)
+    (50, 3, 7, 37),                                     # element path (ragged N)
+    (40, 20, 64, 48),                                   # element path (topk > 16)
+])
+def test_combine_small(T, topk, E, N):
+    rng = np.random.default_rng(T * 7 + N)
+    idx = np.stack([rng.choice(E, topk, replace=False) if topk <= E else rng.integers(0, E, topk)
+                    for _ in range(T)]).astype(np.int32)
+    r = oracle.moe_route(idx, E)
+    R = int(r["offsets"][-1])
+    out = inputs.bf16_bits(inputs.normal_bf16((R, N), 3.0, 70 + N))
+    w = rng.uniform(-1, 1, (T, topk)).astype(np.float32)
+    row_of = r["row_of"].copy()
+    row_of[0, 0] = -1                                   # an unrouted pair contributes nothing
+    check_combine(out, w, row_of, f"combine[{T}x{N} topk={topk}]")
+
+
+def test_combine_full_size():
+    """The MoE down-projection output [32768, 7168] combined into 4096 tokens."""
+    cfg = inputs.CONFIGS[4]
+    T, topk, E, N = cfg["tokens"], cfg["topk"], cfg["experts"], cfg["down"]["N"]
+    g = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    r = oracle.moe_route(g["choice"].astype(np.int32), E)
+    R = int(r["offsets"][-1])
+    out = inputs.bf16_bits(inputs.normal_bf16((R, N), 1.0, inputs.seed_for(4, 5)))
+    w = inputs.routing_weights(T, topk, inputs.seed_for(4, 6))
+    check_combine(out, w, r["row_of"], "combine C4")
+
+
+def test_dispatch_gemm_combine_chain():
+    """route -> quant_scatter -> moe_gemm -> combine on a small MoE, against
+    the oracle chain: y[t] = sum_k w[t,k] * (A_q x B_e^T)[row] within the
+    GEMM bar (1e-2 |ref| + 1e-3 per term) plus the bf16 store of the GEMM
+    output, weighted by |w|."""
+    rng = np.random.default_rng(77)
+    T, topk, E, K, N = 96, 4, 6, 256, 136
+    idx = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = inputs.routing_weights(T, topk, 78)
+    x = inputs.normal_bf16((T, K), 1.0, 79)
+    per_expert = [oracle.weight_quant(inputs.bf16_bits(inputs.normal_bf16((N, K), 0.02, 80 + e)))
+                  for e in range(E)]                   # ragged N: each expert has its own blocks
+    bq = np.stack([p[0] for p in per_expert])
+    bs = np.stack([p[1] for p in per_expert])
+    # oracle chain
+    r = oracle.moe_route(idx, E)
+    R = int(r["offsets"][-1])
+    aq, asc = oracle.moe_quant_scatter(inputs.bf16_bits(x), r["row_of"], R, 0)
+    g = oracle.moe_gemm(aq, asc, bq, bs, r["offsets"])               # [R, N] float64
+    ref = np.zeros((T, N))
+    bar = np.zeros((T, N))
+    for t in range(T):
+        for k in range(topk):
+            row = r["row_of"][t, k]
+            ref[t] += float(w[t, k]) * g[row]
+            bar[t] += abs(float(w[t, k])) * (1.2e-2 * np.abs(g[row]) + 1e-3)
+    # GPU chain, every step through the C ABI
+    off_d, _, row_of_d = fp8bs.moe_route(to_i32(idx), E)
+    q_d, s_d = fp8bs.moe_quant_scatter(x.to(DEV), row_of_d, R, "fp32")
+    b_d = torch.from_numpy(bq).to(DEV)
+    bs_d = torch.from_numpy(bs).to(DEV)
+    out_d = fp8bs.moe_gemm(q_d, s_d, b_d, bs_d, off_d, torch.bfloat16)
+    y = fp8bs.moe_combine(out_d, torch.from_numpy(w).to(DEV), row_of_d, torch.float32)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    bad = np.abs(got - ref) > bar
+    assert not bad.any(), f"chain: {bad.sum()} outside"
