@@ -7,8 +7,8 @@ block-scaled FP8 GEMM with W e4m3 [18432, 7168] (128x128 scales), bf16 out.
 `value` is that step's throughput in TFLOP/s (2*M*N*K per step).  The other
 rows of the hot path -- the decode-shaped linear (GB/s), act_quant in both
 scale formats, weight_dequant, the two small GEMMs of the ue8m0 workload, the
-prefill down-projection and the grouped MoE GEMMs -- are timed as secondary
-rows in the same run.
+prefill down-projection, the grouped MoE GEMMs and the MoE dispatch and
+combine around them -- are timed as secondary rows in the same run.
 
 Inputs are seeded synthetic tensors (block_scaled_fp8_03_amd.inputs), drawn on
 the device and resident in HBM before timing.  Warmup runs at least W steps and
@@ -264,6 +264,47 @@ def bench_moe(steps, warmup, dev, out):
         del bq, bs, y, x, xq, xs
 
 
+def bench_moe_dispatch(steps, warmup, dev, out):
+    """The steps around the expert GEMMs on the MoE workload: the route
+    (counting sort of the 4096 x 8 expert ids), the expert inputs (act_quant of
+    each token written to its 8 routed rows) and the combine of the
+    down-projection output [32768, 7168] into 4096 tokens."""
+    cfg = inputs.CONFIGS[4]
+    E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
+    g = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    idx = torch.from_numpy(g["choice"].astype(np.int32)).to(dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(fp8bs.lib().fp8bs_moe_route_workspace_size(T, topk, E), dtype=torch.uint8,
+                     device=dev)
+    us = timed(lambda c: fp8bs.fp8bs_moe_route(idx, E, offsets, row_token, row_of, ws), 1, steps,
+               warmup)
+    route_bytes = 4 * T * topk + 4 * (E + 1) + 4 * T * topk + 4 * T * topk
+    out[f"moe_route_{T}x{topk}_E{E}"] = row_result("moe route", us, None, route_bytes, "hbm")
+    R = T * topk
+    K, N = cfg["up"]["K"], cfg["down"]["N"]
+    nb = 2 * T * K + R * K + 4 * R * (K // 128) + 4 * T * topk
+    copies = n_copies(nb)
+    xs = [inputs.normal_bf16_device((T, K), 1.0, inputs.seed_for(4, 60 + c), dev) for c in range(copies)]
+    qs = [torch.empty((R, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(copies)]
+    ss = [torch.empty((R, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
+    us = timed(lambda c: fp8bs.fp8bs_moe_quant_scatter(xs[c], row_of, qs[c], ss[c]), copies, steps,
+               warmup)
+    out[f"moe_quant_scatter_{T}x{K}_to_{R}"] = row_result("moe quant_scatter", us, None, nb, "hbm",
+                                                          {"copies": copies})
+    del xs, qs, ss
+    nb = 2 * R * N + 8 * T * topk + 2 * T * N
+    copies = n_copies(nb)
+    outs = [inputs.normal_bf16_device((R, N), 1.0, inputs.seed_for(4, 70 + c), dev) for c in range(copies)]
+    w = torch.from_numpy(inputs.routing_weights(T, topk, inputs.seed_for(4, 6))).to(dev)
+    ys = [torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    us = timed(lambda c: fp8bs.fp8bs_moe_combine(outs[c], w, row_of, ys[c]), copies, steps, warmup)
+    out[f"moe_combine_{R}x{N}_to_{T}"] = row_result("moe combine", us, None, nb, "hbm",
+                                                    {"copies": copies})
+    del outs, ys
+
+
 def cpu_baseline(x_dev, w_dev, budget_s):
     """The oracle on a row sample of the prefill linear: act_quant of the
     sampled rows of x, then all N outputs of each sampled row in binary64, with
@@ -297,7 +338,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
-                    "decode,act_quant,dequant,small,moe,down")
+                    "decode,act_quant,dequant,small,moe,dispatch,down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -334,7 +375,7 @@ def main():
                                                         act_quant_bytes(M, K), "hbm")
     rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
                                                          gemm_bytes(M, N, K), "mfma")
-    sel = set(["decode", "act_quant", "dequant", "small", "moe", "down"]) if args.rows == "all" else (
+    sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "down"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
@@ -352,6 +393,8 @@ def main():
         bench_small_gemms(args.steps, args.warmup, dev, rows)
     if "moe" in sel:
         bench_moe(args.steps, args.warmup, dev, rows)
+    if "dispatch" in sel:
+        bench_moe_dispatch(args.steps, args.warmup, dev, rows)
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_count_kernel(
   const int4* ids4 = (const int4*)ids;
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
     int cnt = 0;
+#pragma unroll 16
     for (int i = 0; i < kRouteChunk / 4; ++i) {        // padding ids are -1: never an expert
       const int4 v = ids4[i];
       cnt += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
@@ -67,15 +68,25 @@ __global__ __launch_bounds__(kScanThreads) void moe_route_scan_kernel(int32_t* _
   __shared__ int32_t carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
+  constexpr int kBatch = 16;                           // column loads in flight per thread
   for (int e0 = 0; e0 < E; e0 += kScanThreads) {
     const int e = e0 + threadIdx.x;
     // exclusive prefix of expert e's column over the chunks; tot = its hits
     int tot = 0;
     if (e < E)
-      for (int c = 0; c < C; ++c) {
-        const int v = hist[(int64_t)c * E + e];
-        hist[(int64_t)c * E + e] = tot;
-        tot += v;
+      for (int c0 = 0; c0 < C; c0 += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < C ? hist[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int x = v[j];
+          v[j] = tot;
+          tot += x;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          if (c0 + j < C) hist[(int64_t)(c0 + j) * E + e] = v[j];
       }
     // exclusive prefix of the totals over the experts of this round
     part[threadIdx.x] = tot;
@@ -89,7 +100,14 @@ __global__ __launch_bounds__(kScanThreads) void moe_route_scan_kernel(int32_t* _
     const int first = carry + part[threadIdx.x] - tot;
     if (e < E) {
       offsets[e] = first;
-      for (int c = 0; c < C; ++c) hist[(int64_t)c * E + e] += first;
+      for (int c0 = 0; c0 < C; c0 += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < C ? hist[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          if (c0 + j < C) hist[(int64_t)(c0 + j) * E + e] = v[j] + first;
+      }
     }
     __syncthreads();                                   // every thread has read carry
     if (threadIdx.x == kScanThreads - 1) carry += part[threadIdx.x];
@@ -98,12 +116,63 @@ __global__ __launch_bounds__(kScanThreads) void moe_route_scan_kernel(int32_t* _
   if (threadIdx.x == 0) offsets[E] = carry;
 }
 
+// Pair-parallel placement of one chunk, for E <= kFusedMaxE.  base[e] (LDS)
+// holds expert e's next free row; wcnt is LDS scratch [4][E].  The chunk goes
+// in rounds of 256 pairs, wave w taking pairs 64w .. 64w+63 of the round.  A
+// pair's row is base[id] + (pairs of the same expert in earlier waves of the
+// round) + (earlier lanes of its own wave with the same expert), found with
+// 63 lane shuffles; the per-wave counts come from LDS atomic adds, whose
+// order does not matter, so the placement is deterministic.
+constexpr int kFusedMaxE = 2048;
+
+__device__ void place_chunk(const int32_t* ids, int n, int64_t p0, int topk, int E, int32_t* base,
+                            int32_t* wcnt, int32_t* __restrict__ row_token,
+                            int32_t* __restrict__ row_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r0 = 0; r0 < kRouteChunk; r0 += kRouteThreads) {
+    const int i = r0 + threadIdx.x;
+    const int id = i < n ? ids[i] : -1;
+    const bool valid = id >= 0 && id < E;
+    int local = 0;
+    for (int d = 1; d < 64; ++d) {
+      const int other = __shfl(id, (lane - d) & 63);
+      local += (lane >= d && other == id) ? 1 : 0;
+    }
+    for (int j = threadIdx.x; j < 4 * E; j += kRouteThreads) wcnt[j] = 0;
+    __syncthreads();
+    if (valid) atomicAdd(&wcnt[wave * E + id], 1);
+    __syncthreads();
+    if (valid) {
+      int pos = base[id] + local;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w * E + id];
+      const int64_t p = p0 + i;
+      row_token[pos] = (int32_t)(p / topk);
+      row_of[p] = pos;
+    } else if (i < n) {
+      row_of[p0 + i] = -1;
+    }
+    __syncthreads();                                  // every lane has read base and wcnt
+    for (int e = threadIdx.x; e < E; e += kRouteThreads)
+      base[e] += wcnt[e] + wcnt[E + e] + wcnt[2 * E + e] + wcnt[3 * E + e];
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_place_kernel(
     const int32_t* __restrict__ idx, int64_t P, int topk, int E, const int32_t* __restrict__ first,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
   __shared__ __attribute__((aligned(16))) int32_t ids[kRouteChunk];
+  __shared__ int32_t base[kFusedMaxE];
+  __shared__ int32_t wcnt[4 * kFusedMaxE];
   const int n = load_chunk_ids(idx, P, ids);
   const int64_t p0 = (int64_t)blockIdx.x * kRouteChunk;
+  if (E <= kFusedMaxE) {
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) base[e] = first[(int64_t)blockIdx.x * E + e];
+    __syncthreads();
+    place_chunk(ids, n, p0, topk, E, base, wcnt, row_token, row_of);
+    return;
+  }
+  // many experts: one thread per expert walks the chunk in order
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
     int pos = first[(int64_t)blockIdx.x * E + e];
     for (int i = 0; i < n; ++i)
@@ -116,6 +185,63 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_place_kernel(
   }
   for (int i = threadIdx.x; i < n; i += kRouteThreads)
     if (ids[i] < 0 || ids[i] >= E) row_of[p0 + i] = -1;
+}
+
+// Passes 2 and 3 in one launch (when E <= kFusedMaxE and C * E is small):
+// every placement workgroup reads the whole [C][E] count table (from L2),
+// forms each expert's total and the count of its own earlier chunks, scans the
+// totals over the experts itself, and places its chunk.  Workgroup 0 also
+// writes offsets.  The count table is only read, so the workgroups need no
+// ordering among themselves.
+constexpr int64_t kFusedMaxTable = 1 << 16;
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_scan_place_kernel(
+    const int32_t* __restrict__ idx, int64_t P, int topk, int E, int C,
+    const int32_t* __restrict__ hist, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
+  __shared__ __attribute__((aligned(16))) int32_t ids[kRouteChunk];
+  __shared__ int32_t base[kFusedMaxE];
+  __shared__ int32_t wcnt[4 * kFusedMaxE];
+  __shared__ int32_t part[kRouteThreads];
+  __shared__ int32_t carry;
+  const int c = blockIdx.x;
+  const int n = load_chunk_ids(idx, P, ids);
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  constexpr int kBatch = 32;
+  for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
+    const int e = e0 + threadIdx.x;
+    int tot = 0, pre = 0;                               // all chunks; chunks before c
+    if (e < E)
+      for (int c0 = 0; c0 < C; c0 += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < C ? hist[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          tot += v[j];
+          pre += c0 + j < c ? v[j] : 0;
+        }
+      }
+    part[threadIdx.x] = tot;
+    __syncthreads();
+    for (int d = 1; d < kRouteThreads; d <<= 1) {
+      const int v = threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const int first = carry + part[threadIdx.x] - tot;
+    if (e < E) {
+      base[e] = first + pre;
+      if (c == 0) offsets[e] = first;
+    }
+    __syncthreads();                                   // every thread has read carry
+    if (threadIdx.x == kRouteThreads - 1) carry += part[threadIdx.x];
+    __syncthreads();
+  }
+  if (c == 0 && threadIdx.x == 0) offsets[E] = carry;
+  place_chunk(ids, n, (int64_t)c * kRouteChunk, topk, E, base, wcnt, row_token, row_of);
 }
 
 int64_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -133,6 +259,11 @@ hipError_t launch_moe_route(const int32_t* indices, int64_t T, int64_t topk, int
     moe_route_count_kernel<<<dim3(C), dim3(kRouteThreads), 0, stream>>>(indices, P, (int)E, hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (E <= kFusedMaxE && (int64_t)C * E <= kFusedMaxTable) {
+      moe_route_scan_place_kernel<<<dim3(C), dim3(kRouteThreads), 0, stream>>>(
+          indices, P, (int)topk, (int)E, C, hist, offsets, row_token, row_of);
+      return hipGetLastError();
+    }
   }
   moe_route_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, stream>>>(hist, C, (int)E, offsets);
   hipError_t err = hipGetLastError();
@@ -145,42 +276,49 @@ hipError_t launch_moe_route(const int32_t* indices, int64_t T, int64_t topk, int
 // ----------------------------------------------------------------------------
 // combine
 // ----------------------------------------------------------------------------
-// Vector path (N % 8 == 0, 16-byte aligned buffers): a thread owns 8
-// consecutive columns of one token, issues the topk row loads (16 bytes of
-// bf16 each) before using any, and sums w * out in fp32 in slot order.
+// Vector path (N % 8 == 0, 16-byte aligned buffers, topk <= KMAX, R*N*2 <
+// 2^32): a thread owns 8 consecutive columns of one token and issues all its
+// row loads (16 bytes of bf16 each) before using any.  Slots k >= topk and
+// pairs outside [0, R) load through an out-of-range buffer offset, which
+// returns zeros without touching memory, and carry weight 0, so every load is
+// unconditional; the sum runs in fp32 in slot order.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineMaxTopk = 16;
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-template <bool OUT_F32>
+template <int KMAX, bool OUT_F32>
 __global__ __launch_bounds__(kCombineThreads) void moe_combine_vec_kernel(
-    const uint4* __restrict__ out, const float* __restrict__ w, const int32_t* __restrict__ row_of,
+    const void* __restrict__ out, const float* __restrict__ w, const int32_t* __restrict__ row_of,
     void* __restrict__ y, int64_t T, int topk, int64_t R, int64_t nv) {
   const int64_t i = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
   if (i >= T * nv) return;
   const int64_t t = i / nv, v = i - t * nv;
-  uint4 o[kCombineMaxTopk];
-  float wk[kCombineMaxTopk];
+  // raw buffer over out (R rows of nv 16-byte vectors), 32-bit data format
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(out), (short)0, (int)(uint32_t)(R * nv * 16), 0x00020000);
+  int r[KMAX];
+  float wk[KMAX];
 #pragma unroll
-  for (int k = 0; k < kCombineMaxTopk; ++k) {
-    wk[k] = 0.0f;
-    o[k] = make_uint4(0, 0, 0, 0);
-    if (k < topk) {
-      const int64_t r = row_of[t * topk + k];
-      if (r >= 0 && r < R) {
-        wk[k] = w[t * topk + k];
-        o[k] = out[r * nv + v];
-      }
-    }
+  for (int k = 0; k < KMAX; ++k) {
+    const int kk = k < topk ? k : topk - 1;              // in-range index for the load
+    r[k] = row_of[t * topk + kk];
+    wk[k] = w[t * topk + kk];
+  }
+  v4i_t o[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const bool ok = k < topk && r[k] >= 0 && r[k] < R;
+    const uint32_t off = ok ? (uint32_t)(((int64_t)r[k] * nv + v) * 16) : 0xF0000000u;
+    o[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    if (!ok) wk[k] = 0.0f;
   }
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int k = 0; k < kCombineMaxTopk; ++k) {
-    if (k >= topk) break;
-    const uint32_t h[4] = {o[k].x, o[k].y, o[k].z, o[k].w};
+  for (int k = 0; k < KMAX; ++k) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = __builtin_fmaf(wk[k], bf16_lo(h[j]), acc[2 * j]);
-      acc[2 * j + 1] = __builtin_fmaf(wk[k], bf16_hi(h[j]), acc[2 * j + 1]);
+      const uint32_t h = (uint32_t)o[k][j];
+      acc[2 * j] = __builtin_fmaf(wk[k], bf16_lo(h), acc[2 * j]);
+      acc[2 * j + 1] = __builtin_fmaf(wk[k], bf16_hi(h), acc[2 * j + 1]);
     }
   }
   if (OUT_F32) {
@@ -218,17 +356,22 @@ hipError_t launch_moe_combine(const void* out, const float* w, const int32_t* ro
                               int64_t T, int64_t topk, int64_t R, int64_t N, bool out_f32,
                               hipStream_t stream) {
   if (T == 0 || N == 0) return hipSuccess;
-  const bool vec = N % 8 == 0 && topk <= kCombineMaxTopk && ((uintptr_t)out & 15) == 0 &&
-                   ((uintptr_t)y & 15) == 0;
+  const bool vec = N % 8 == 0 && topk <= 16 && ((uintptr_t)out & 15) == 0 &&
+                   ((uintptr_t)y & 15) == 0 && R * N * 2 < ((int64_t)1 << 32) - ((int64_t)1 << 28);
   if (vec) {
     const int64_t nv = N / 8, total = T * nv;
-    const dim3 grid((unsigned)((total + kCombineThreads - 1) / kCombineThreads));
-    if (out_f32)
-      moe_combine_vec_kernel<true><<<grid, dim3(kCombineThreads), 0, stream>>>(
-          (const uint4*)out, w, row_of, y, T, (int)topk, R, nv);
-    else
-      moe_combine_vec_kernel<false><<<grid, dim3(kCombineThreads), 0, stream>>>(
-          (const uint4*)out, w, row_of, y, T, (int)topk, R, nv);
+    const dim3 grid((unsigned)((total + kCombineThreads - 1) / kCombineThreads)), block(kCombineThreads);
+    if (topk <= 8) {
+      if (out_f32)
+        moe_combine_vec_kernel<8, true><<<grid, block, 0, stream>>>(out, w, row_of, y, T, (int)topk, R, nv);
+      else
+        moe_combine_vec_kernel<8, false><<<grid, block, 0, stream>>>(out, w, row_of, y, T, (int)topk, R, nv);
+    } else {
+      if (out_f32)
+        moe_combine_vec_kernel<16, true><<<grid, block, 0, stream>>>(out, w, row_of, y, T, (int)topk, R, nv);
+      else
+        moe_combine_vec_kernel<16, false><<<grid, block, 0, stream>>>(out, w, row_of, y, T, (int)topk, R, nv);
+    }
   } else {
     const int64_t total = T * N;
     const dim3 grid((unsigned)((total + kCombineThreads - 1) / kCombineThreads));

@@ -41,8 +41,9 @@ def check_route(idx: np.ndarray, E: int, what: str):
 @pytest.mark.parametrize("T,topk,E,seed", [
     (1, 1, 1, 0), (5, 3, 4, 1), (100, 8, 16, 2),      # repeats within a token allowed
     (700, 8, 300, 3),                                 # experts > threads of a workgroup
-    (2000, 2, 3000, 4),                               # experts > one scan round
+    (2000, 2, 3000, 4),                               # experts > one scan round (3 launches)
     (513, 1, 7, 5),                                   # one pair past a chunk boundary
+    (20000, 8, 256, 6),                               # count table too big to fuse (3 launches)
 ])
 def test_route_random(T, topk, E, seed):
     rng = np.random.default_rng(seed)
