@@ -71,6 +71,8 @@ def _load():
     lib.orc_gemm_points.argtypes = [P, P, P, P, I64, P, P, I64, P]
     lib.orc_moe_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     lib.orc_moe_gemm_points.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, I64, P]
+    lib.orc_w8a16_gemm.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.orc_w8a16_gemm_points.argtypes = [P, P, P, I64, I64, P, P, I64, P]
     lib.orc_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.orc_moe_route.restype = I64
     lib.orc_moe_quant_scatter.argtypes = [P, I64, I64, ctypes.c_int, P, I64, I64, P, P]
@@ -241,6 +243,39 @@ def moe_gemm_points(a, a_s, b, b_s, offsets, rows, cols) -> np.ndarray:
     out = np.empty(rows.shape, dtype=np.float64)
     _load().orc_moe_gemm_points(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(offsets), E, N, K,
                                 _ptr(rows), _ptr(cols), rows.size, _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------ the BF16 path
+
+def w8a16_gemm(x_bf16_bits: np.ndarray, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """C = x . weight_dequant(q, s)^T in binary64: x bf16 bits uint16 [M, K],
+    q e4m3 [N, K], s float32 [ceil(N/128), ceil(K/128)] (Admin guide 6.3, the
+    gemm_impl "bf16" path: dequantise, then a BF16 linear)."""
+    x = _c(x_bf16_bits, np.uint16)
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    M, K = x.shape
+    N, K2 = q.shape
+    if K != K2 or s.shape != (-(-N // BLOCK), -(-K // BLOCK)):
+        raise ValueError("x [M, K], q [N, K], s [ceil(N/128), ceil(K/128)]")
+    c = np.empty((M, N), dtype=np.float64)
+    _load().orc_w8a16_gemm(_ptr(x), _ptr(q), _ptr(s), M, N, K, _ptr(c))
+    return c
+
+
+def w8a16_gemm_points(x_bf16_bits, q, s, rows, cols) -> np.ndarray:
+    x = _c(x_bf16_bits, np.uint16)
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < M and cols.min() >= 0 and cols.max() < N)
+    out = np.empty(rows.shape, dtype=np.float64)
+    _load().orc_w8a16_gemm_points(_ptr(x), _ptr(q), _ptr(s), N, K, _ptr(rows), _ptr(cols), rows.size,
+                                  _ptr(out))
     return out
 
 

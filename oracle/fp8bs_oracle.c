@@ -323,6 +323,42 @@ void orc_moe_gemm_points(const uint8_t* a, const float* a_s, const uint8_t* b, c
 }
 
 /* ------------------------------------------------------------------------ */
+/* The BF16 path of the linear (Admin guide 6.3: with gemm_impl "bf16" the   */
+/* FP8 weight is dequantised by weight_dequant (8.5.2) and the product runs   */
+/* as a BF16 F.linear): C[m, n] = sum_k x[m, k] * Wd[n, k], x bf16 [M, K],    */
+/* Wd = weight_dequant(q, s) bf16 [N, K].  Each product of two bf16 values is */
+/* exact in binary64 (8 + 8 significant bits) and the sum of K of them is    */
+/* formed in binary64 in k order (exact while K * 2^16 * 2^(e-range) fits;   */
+/* in any case within a few binary64 ulps).                                  */
+/* ------------------------------------------------------------------------ */
+static double w8a16_point(const uint16_t* x, const uint16_t* wd, int64_t K, int64_t m, int64_t n) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += (double)orc_bf16_to_f32(x[m * K + k]) * (double)orc_bf16_to_f32(wd[n * K + k]);
+    return acc;
+}
+
+void orc_w8a16_gemm(const uint16_t* x, const uint8_t* q, const float* s, int64_t M, int64_t N,
+                    int64_t K, double* c) {
+    uint16_t* wd = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N * K > 0 ? N * K : 1));
+    orc_weight_dequant(q, s, N, K, wd);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) c[m * N + n] = w8a16_point(x, wd, K, m, n);
+    free(wd);
+}
+
+/* The same at (row, col) points. */
+void orc_w8a16_gemm_points(const uint16_t* x, const uint8_t* q, const float* s, int64_t N, int64_t K,
+                           const int64_t* rows, const int64_t* cols, int64_t npts, double* out) {
+    uint16_t* wd = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N * K > 0 ? N * K : 1));
+    orc_weight_dequant(q, s, N, K, wd);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npts; ++i) out[i] = w8a16_point(x, wd, K, rows[i], cols[i]);
+    free(wd);
+}
+
+/* ------------------------------------------------------------------------ */
 /* MoE dispatch and combine around the expert GEMMs (Admin guide 6.4 and     */
 /* 8.4: per-expert hit counts by bincount; for each expert with hits, the     */
 /* (token, slot) pairs whose routed expert it is, in token order as          */

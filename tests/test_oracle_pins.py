@@ -548,3 +548,62 @@ def test_moe_combine_one_hot_and_linear(orc):
     w3 = w2.copy()
     w3[:, 0] = 0
     assert np.array_equal(orc.moe_combine(out, w2, row_of), orc.moe_combine(out, w3, r["row_of"]))
+
+
+# ----------------------------------------------------------- the BF16 path
+
+def _bf16_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (7, 130, 256), (33, 64, 384)])
+def test_w8a16_matches_torch_dequant_matmul(orc, M, N, K):
+    """Library special case: torch's bfloat16 cast of the float32 product
+    decode(q)*s (the pages' weight_dequant, computed by torch from the code
+    table) and a float64 matmul with the bf16 activations."""
+    rng = np.random.default_rng(M + N + K)
+    x = inputs.bf16_bits(inputs.normal_bf16((M, K), 1.0, M * 3 + K))
+    q = _rand_codes(rng, (N, K))
+    s = (2.0 ** rng.uniform(-12, 2, (-(-N // 128), K // 128))).astype(np.float32)
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+    sf = torch.from_numpy(np.repeat(np.repeat(s, 128, 0), 128, 1)[:N, :K])
+    wd = (dec * sf).to(torch.bfloat16).double().numpy()
+    ref = _bf16_f64(x) @ wd.T
+    got = orc.w8a16_gemm(x, q, s)
+    bound = np.abs(_bf16_f64(x)) @ np.abs(wd).T
+    assert np.all(np.abs(got - ref) <= 1e-14 * bound + 1e-300)
+
+
+def test_w8a16_closed_forms(orc):
+    """Codes of 1.0 (0x38) with unit scales give the row sums of x; a one-hot
+    row of x picks out the dequantised weight column; the result equals the
+    block-scaled FP8 GEMM of the same operands when x is exactly an e4m3 value
+    with scale 1 and the weight scales are powers of two (both exact)."""
+    M, N, K = 5, 9, 256
+    x = inputs.bf16_bits(inputs.normal_bf16((M, K), 1.0, 11))
+    q = np.full((N, K), 0x38, dtype=np.uint8)
+    s = np.ones((1, 2), dtype=np.float32)
+    c = orc.w8a16_gemm(x, q, s)
+    assert np.array_equal(c, np.repeat(_bf16_f64(x).sum(1, keepdims=True), N, 1))
+    rng = np.random.default_rng(3)
+    q = _rand_codes(rng, (N, K))
+    s = (2.0 ** rng.integers(-8, 3, (1, 2))).astype(np.float32)
+    xo = np.zeros((1, K), dtype=np.uint16)
+    xo[0, 77] = 0x3F80                                   # 1.0 in bf16
+    wd = orc.weight_dequant(q, s)
+    assert np.array_equal(orc.w8a16_gemm(xo, q, s)[0], _bf16_f64(wd)[:, 77])
+    a = _rand_codes(rng, (M, K))
+    a_bits = inputs.bf16_bits(torch.from_numpy(orc.e4m3_decode_array(a)).float().to(torch.bfloat16))
+    ones = np.ones((M, K // 128), dtype=np.float32)
+    assert np.array_equal(orc.w8a16_gemm(a_bits, q, s), orc.gemm(a, ones, q, s))
+
+
+def test_w8a16_points_equal_full(orc):
+    rng = np.random.default_rng(5)
+    M, N, K = 20, 140, 384
+    x = inputs.bf16_bits(inputs.normal_bf16((M, K), 1.0, 12))
+    q = _rand_codes(rng, (N, K))
+    s = rng.uniform(0.01, 1, (2, 3)).astype(np.float32)
+    full = orc.w8a16_gemm(x, q, s)
+    r, c = rng.integers(0, M, 30), rng.integers(0, N, 30)
+    assert np.array_equal(orc.w8a16_gemm_points(x, q, s, r, c), full[r, c])
