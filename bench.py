@@ -7,8 +7,9 @@ block-scaled FP8 GEMM with W e4m3 [18432, 7168] (128x128 scales), bf16 out.
 `value` is that step's throughput in TFLOP/s (2*M*N*K per step).  The other
 rows of the hot path -- the decode-shaped linear (GB/s), act_quant in both
 scale formats, weight_dequant, the two small GEMMs of the ue8m0 workload, the
-prefill down-projection, the grouped MoE GEMMs and the MoE dispatch and
-combine around them -- are timed as secondary rows in the same run.
+prefill down-projection, the grouped MoE GEMMs, the MoE dispatch and
+combine around them, and the BF16 path (weight dequantised inside a bf16
+GEMM) -- are timed as secondary rows in the same run.
 
 Inputs are seeded synthetic tensors (block_scaled_fp8_03_amd.inputs), drawn on
 the device and resident in HBM before timing.  Warmup runs at least W steps and
@@ -305,6 +306,26 @@ def bench_moe_dispatch(steps, warmup, dev, out):
     del outs, ys
 
 
+def bench_w8a16(steps, warmup, dev, out):
+    """The BF16 path of the linear (weight dequantised in registers, bf16
+    MFMA) on the prefill and decode shapes, against the bf16 MFMA peak (prefill)
+    and HBM (decode)."""
+    for (M, N, K, cfg, bound) in [(4096, 18432, 7168, 3, "mfma_bf16"), (32, 18432, 7168, 2, "hbm")]:
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 20), dev)
+        nb = 2 * M * K + N * K + 4 * (-(-N // 128)) * (K // 128) + 2 * M * N
+        copies = n_copies(N * K) if bound == "hbm" else 1
+        ws = [quantised_weight(N, K, inputs.seed_for(cfg, 21) + 100 * c, dev) for c in range(copies)]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda c: fp8bs.fp8bs_w8a16_gemm(x, ws[c][0], ws[c][1], y), copies, steps, warmup)
+        r = row_result(f"w8a16 gemm {M}x{N}x{K}", us, 2 * M * N * K, nb,
+                       "hbm" if bound == "hbm" else None, {"copies": copies})
+        if bound == "mfma_bf16":
+            r["bound"] = "mfma_bf16"
+            r["frac"] = round(2 * M * N * K / us / 1e6 / PEAK_BF16_TFLOPS, 4)
+        out[f"w8a16_gemm_{M}x{N}x{K}"] = r
+        del ws, x, y
+
+
 def cpu_baseline(x_dev, w_dev, budget_s):
     """The oracle on a row sample of the prefill linear: act_quant of the
     sampled rows of x, then all N outputs of each sampled row in binary64, with
@@ -338,7 +359,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
-                    "decode,act_quant,dequant,small,moe,dispatch,down")
+                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -375,7 +396,7 @@ def main():
                                                         act_quant_bytes(M, K), "hbm")
     rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
                                                          gemm_bytes(M, N, K), "mfma")
-    sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "down"]) if args.rows == "all" else (
+    sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "w8a16", "down"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
@@ -395,6 +416,8 @@ def main():
         bench_moe(args.steps, args.warmup, dev, rows)
     if "dispatch" in sel:
         bench_moe_dispatch(args.steps, args.warmup, dev, rows)
+    if "w8a16" in sel:
+        bench_w8a16(args.steps, args.warmup, dev, rows)
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6

@@ -6,11 +6,12 @@ library's HIP kernels.  PyTorch provides device memory and streams.
 
 Raw entry points carry the C names and take caller-allocated outputs:
 ``fp8bs_act_quant``, ``fp8bs_weight_quant``, ``fp8bs_weight_dequant``,
-``fp8bs_gemm``, ``fp8bs_moe_gemm`` and the MoE dispatch/combine steps
+``fp8bs_gemm``, ``fp8bs_moe_gemm``, the BF16 path ``fp8bs_w8a16_gemm`` and
+the MoE dispatch/combine steps
 ``fp8bs_moe_route``, ``fp8bs_moe_quant_scatter``, ``fp8bs_moe_combine``.
 Allocating conveniences: ``act_quant``, ``weight_quant``, ``weight_dequant``,
-``fp8_gemm``, ``moe_gemm``, ``linear``, ``moe_route``, ``moe_quant_scatter``,
-``moe_combine``.
+``fp8_gemm``, ``moe_gemm``, ``linear``, ``w8a16_gemm``, ``moe_route``,
+``moe_quant_scatter``, ``moe_combine``.
 
 The operations follow the DeepSeek-V3 inference pages ("DeepSeek-V3
 Administrator & Developer Guide", sections 6.3, 6.4, 8.5.1-8.5.3; "DeepSeek-V3
@@ -27,7 +28,8 @@ import torch
 __all__ = [
     "SCALE_FP32", "SCALE_UE8M0", "OUT_BF16", "OUT_F32", "Fp8bsError", "library_path", "lib",
     "fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
-    "fp8bs_moe_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter", "fp8bs_moe_combine",
+    "fp8bs_moe_gemm", "fp8bs_w8a16_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter",
+    "fp8bs_moe_combine", "w8a16_gemm",
     "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm", "linear", "moe_route",
     "moe_quant_scatter", "moe_combine",
 ]
@@ -69,13 +71,15 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_weight_dequant.argtypes = [P, P, P, I64, I64, P]
     L.fp8bs_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     L.fp8bs_moe_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, P]
+    L.fp8bs_w8a16_gemm.argtypes = [P, P, P, P, I64, I64, I64, I, P]
     L.fp8bs_moe_route_workspace_size.argtypes = [I64, I64, I64]
     L.fp8bs_moe_route_workspace_size.restype = I64
     L.fp8bs_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
     L.fp8bs_moe_quant_scatter.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     L.fp8bs_moe_combine.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     for fn in ("fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
-               "fp8bs_moe_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter", "fp8bs_moe_combine"):
+               "fp8bs_moe_gemm", "fp8bs_w8a16_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter",
+               "fp8bs_moe_combine"):
         getattr(L, fn).restype = I
     _lib = L
     return L
@@ -184,6 +188,19 @@ def fp8bs_moe_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: tor
           _need(b, _F8, "b"), _need(b_s, (torch.float32,), "b_s"),
           _need(offsets, (torch.int32,), "offsets"),
           _need(c, (torch.bfloat16, torch.float32), "c"), R, E, N, K, _out_code(c), _stream(a))
+
+
+def fp8bs_w8a16_gemm(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, c: torch.Tensor) -> None:
+    """The BF16 path: C [M, N] = x bf16 [M, K] . weight_dequant(w e4m3 [N, K], w_s)^T."""
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2 or K % BLOCK:
+        raise ValueError("x and w need the same K, a multiple of 128")
+    if tuple(w_s.shape) != (-(-N // BLOCK), K // BLOCK) or tuple(c.shape) != (M, N):
+        raise ValueError("scale or output shape mismatch")
+    _call("fp8bs_w8a16_gemm", _need(x, (torch.bfloat16,), "x"), _need(w, _F8, "w"),
+          _need(w_s, (torch.float32,), "w_s"), _need(c, (torch.bfloat16, torch.float32), "c"),
+          M, N, K, _out_code(c), _stream(x))
 
 
 def fp8bs_moe_route(indices: torch.Tensor, E: int, offsets: torch.Tensor, row_token: torch.Tensor,
@@ -310,3 +327,12 @@ def moe_combine(out: torch.Tensor, w: torch.Tensor, row_of: torch.Tensor,
     y = torch.empty((w.shape[0], out.shape[1]), dtype=out_dtype, device=out.device)
     fp8bs_moe_combine(out, w, row_of, y)
     return y
+
+
+def w8a16_gemm(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """x bf16 [..., K] times the dequantised FP8 weight [N, K]^T -> [..., N]."""
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    c = torch.empty((x2.shape[0], w.shape[0]), dtype=out_dtype, device=x.device)
+    fp8bs_w8a16_gemm(x2, w, w_s, c)
+    return c.view(*x.shape[:-1], w.shape[0])

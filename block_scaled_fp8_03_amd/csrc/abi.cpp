@@ -149,6 +149,27 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
                                           out_dtype == FP8BS_OUT_F32, (hipStream_t)stream));
 }
 
+int fp8bs_w8a16_gemm(const void* x_bf16, const void* w_e4m3, const float* w_s, void* c, int64_t M,
+                     int64_t N, int64_t K, int out_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ENUM;
+  if (M > kLimitInt || N > kLimitInt || K > kLimitInt) return FP8BS_ERR_SHAPE;
+  const int64_t nx = mul(M, K), nw = mul(N, K), nc = mul(M, N);
+  if (nx < 0 || nw < 0 || nc < 0 || mul(M + 256, 2 * K) >= kLimit32 || mul(N + 256, K) >= kLimit32 ||
+      mul(nc, 4) < 0 || mul(cdiv(M, 256), cdiv(N, 256)) > kLimitInt)
+    return FP8BS_ERR_SHAPE;
+  if (nc == 0) return FP8BS_OK;
+  if (!x_bf16 || !w_e4m3 || !w_s || !c) return FP8BS_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w_e4m3, 16) || !aligned(c, 16) || !aligned(w_s, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t cb = nc * (out_dtype == FP8BS_OUT_F32 ? 4 : 2);
+  const int64_t nws = cdiv(N, 128) * (K / 128) * 4;
+  if (overlap(c, cb, x_bf16, 2 * nx) || overlap(c, cb, w_e4m3, nw) || overlap(c, cb, w_s, nws))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_w8a16_gemm(x_bf16, w_e4m3, w_s, c, M, N, K,
+                                            out_dtype == FP8BS_OUT_F32, (hipStream_t)stream));
+}
+
 int64_t fp8bs_moe_route_workspace_size(int64_t T, int64_t topk, int64_t E) {
   if (T < 0 || topk < 1 || E < 1 || E > kLimitInt) return -1;
   const int64_t P = mul(T, topk);

@@ -597,6 +597,178 @@ gemm_decode_kernel(GemmParams p, int rows) {
 }
 
 // ----------------------------------------------------------------------------
+// BF16 path (W8A16): C = x . weight_dequant(W)^T with x bf16, W e4m3 + 128x128
+// block scales ("DeepSeek-V3 Administrator & Developer Guide" 6.3: with
+// gemm_impl "bf16" the FP8 weight is dequantised (8.5.2) and the linear runs
+// in BF16).  The dequantised weight is never stored: each wave decodes the
+// weight codes of its fragments in registers -- RN32(decode(q) * s), then
+// bf16 round-to-nearest-even, exactly the weight_dequant rounding -- and feeds
+// them to v_mfma_f32_16x16x32_bf16, which accumulates in fp32 (no per-block
+// fold: the scale is inside the dequantised operand).
+//
+// Workgroup: 8 waves, 256 (m) x 256 (n) tile, wave 128 x 64 as in the FP8
+// tile kernel.  A stage is a 64-wide K slice: [x 256 rows x 128 bytes][W 256
+// rows x 64 bytes][b_s per wave]; three stages (150 KB).  K mapping of one
+// slice: MFMA step s (0, 1), lane group g takes K [16g + 8s, 16g + 8s + 8), so
+// a lane's weight codes for both steps are the 16 contiguous bytes [16g,
+// 16g + 16) of its row, and its x values for step s the 16 bytes at 32g + 16s.
+// The 128-byte x rows use the swizzle of the FP8 kernel; the 64-byte weight
+// rows put chunk c of row r at c ^ ((r >> 1) & 2), which keeps the weight
+// fragment reads conflict-free under the same bank rule.
+__device__ __forceinline__ int swz64(int r) { return (r >> 1) & 2; }
+
+// 8 e4m3 codes (byte order = element order) times s -> 8 bf16 (two roundings)
+__device__ __forceinline__ v8bf dequant8_bf16(uint32_t w0, uint32_t w1, float sc) {
+  const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const v2f d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+  const v4u_t u = {pack2_bf16(__fmul_rn(a.x, sc), __fmul_rn(a.y, sc)),
+                   pack2_bf16(__fmul_rn(b.x, sc), __fmul_rn(b.y, sc)),
+                   pack2_bf16(__fmul_rn(c.x, sc), __fmul_rn(c.y, sc)),
+                   pack2_bf16(__fmul_rn(d.x, sc), __fmul_rn(d.y, sc))};
+  return __builtin_bit_cast(v8bf, u);
+}
+
+template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC, bool OUT_F32>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))
+w8a16_tile_kernel(GemmParams p) {
+  constexpr int WAVES_M = BM / WM;
+  static_assert(WAVES_M * (BN / WN) == NW && (NW == 4 || NW == 8), "4 or 8 waves");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range lies in one weight block");
+  constexpr int MT = WM / 16, NT = WN / 16;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 64, BS_BYTES = NW * 256;
+  constexpr int STAGE = A_BYTES + B_BYTES + BS_BYTES;
+  constexpr int A_LOADS = A_BYTES / (NW * 1024), B_LOADS = B_BYTES / (NW * 1024);
+  constexpr int LPS = A_LOADS + B_LOADS + 1;
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile shape");
+  static_assert(OCC * ST * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int K = p.K, N = p.N;
+  const int nks = K / 64;                                    // 64-wide K slices
+  const int nbk = K / 128;
+
+  int m_base, n_base;
+  {
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    constexpr int GM = 4;
+    const int group = GM * p.num_n;
+    const int gid = t / group, first_m = gid * GM;
+    const int gsz = min(p.num_m - first_m, GM);
+    const int in = t % group;
+    m_base = (first_m + in % gsz) * BM;
+    n_base = (in / gsz) * BN;
+  }
+
+  const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)p.rows * K * 2));
+  const v4i b_rsrc = make_rsrc(p.b, (uint32_t)((int64_t)N * K));
+  const v4i bs_rsrc = make_rsrc(p.b_s, (uint32_t)((int64_t)((N + 127) / 128) * nbk * 4));
+  // x: load i of this wave covers rows 8 (NW i + wave) .. +7, 8 lanes per row
+  const int arow = 8 * wave + (lane >> 3);
+  const uint32_t a_voff = (uint32_t)(m_base + arow) * (uint32_t)(2 * K) + 16 * ((lane & 7) ^ swz<2>(arow));
+  const uint32_t a_step = 8u * NW * (uint32_t)(2 * K);
+  // W: load i covers rows 16 (NW i + wave) .. +15, 4 lanes per row
+  const int brow = 16 * wave + (lane >> 2);
+  const uint32_t b_voff = (uint32_t)(n_base + brow) * (uint32_t)K + 16 * ((lane & 3) ^ swz64(brow));
+  const uint32_t b_step = 16u * NW * (uint32_t)K;
+  const uint32_t bs_voff = (uint32_t)((n_base + wn * WN) / 128) * nbk * 4;
+  const uint32_t smem_lds = lds_addr(smem);
+
+  auto issue = [&](int ks, int st) {
+    const uint32_t base = smem_lds + st * STAGE + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      dma_b128(a_rsrc, base + i * NW * 1024, a_voff + i * a_step + (uint32_t)ks * 128);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      dma_b128(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * b_step + (uint32_t)ks * 64);
+    dma_b32(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, bs_voff + (ks / 2) * 4);
+  };
+
+  v4f acc[NT][MT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  const int g = lane >> 4, r16 = lane & 15;
+
+#pragma unroll
+  for (int s0 = 0; s0 < ST - 1; ++s0)
+    if (s0 < nks) issue(s0, s0);
+
+  for (int ks = 0; ks < nks; ++ks) {
+    const int st = ks % ST;
+    if (ks + ST - 2 < nks) wait_vmcnt<(ST - 2) * LPS>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (ks + ST - 1 < nks) issue(ks + ST - 1, (ks + ST - 1) % ST);
+
+    const uint8_t* at = smem + st * STAGE;
+    const uint8_t* bt = at + A_BYTES;
+    const float bsv = ((const float*)(at + A_BYTES + B_BYTES))[wave * 64];
+    v8bf bf[NT][2];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int row = wn * WN + 16 * j + r16;
+      const uint4 w = *(const uint4*)(bt + row * 64 + ((g ^ swz64(row)) << 4));
+      bf[j][0] = dequant8_bf16(w.x, w.y, bsv);
+      bf[j][1] = dequant8_bf16(w.z, w.w, bsv);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int ml = wm * WM + 16 * t + r16;
+      const int sw = swz<2>(ml);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const v8bf af = __builtin_bit_cast(v8bf, *(const uint4*)(at + ml * 128 + (((2 * g + s) ^ sw) << 4)));
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j][s], af, acc[j][t], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds C[m][n .. n+3] for each (j, t)
+  const bool vec_ok = (N % 4) == 0;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = m_base + wm * WM + 16 * t + r16;
+    if (m >= p.rows) continue;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n_base + wn * WN + 16 * j + 4 * g;
+      if (n >= N) continue;
+      if (OUT_F32) {
+        float* cp = (float*)p.c + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *(float4*)cp = make_float4(acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]);
+        } else {
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) cp[r] = acc[j][t][r];
+        }
+      } else {
+        uint16_t* cp = (uint16_t*)p.c + (int64_t)m * N + n;
+        const uint32_t lo = pack2_bf16(acc[j][t][0], acc[j][t][1]);
+        const uint32_t hi = pack2_bf16(acc[j][t][2], acc[j][t][3]);
+        if (vec_ok && n + 3 < N) {
+          *(uint2*)cp = make_uint2(lo, hi);
+        } else {
+          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
+                                 (uint16_t)(hi >> 16)};
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) cp[r] = h[r];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
 namespace {
@@ -725,6 +897,34 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   p.num_m = (int)(E * ((kMoeSplit + BM - 1) / BM));
   p.num_n = (int)((N + BN - 1) / BN);
   return run_tile<BM, BN, 64, 64, 3, 4, 2, true>(p, out_f32, p.num_m * p.num_n, stream);
+}
+
+template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC>
+hipError_t run_w8a16(GemmParams p, bool out_f32, hipStream_t stream) {
+  p.num_m = (int)((p.rows + BM - 1) / BM);
+  p.num_n = (int)((p.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(p.num_m * p.num_n)), block(NW * 64);
+  if (out_f32)
+    w8a16_tile_kernel<BM, BN, WM, WN, NW, ST, OCC, true><<<grid, block, 0, stream>>>(p);
+  else
+    w8a16_tile_kernel<BM, BN, WM, WN, NW, ST, OCC, false><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+// Tile choice: decode-sized M streams the weight through 64-column tiles
+// (two workgroups per CU, six stages); GEMMs whose 256 x 256 tiles cannot
+// fill the CUs use 128 x 128 tiles; the rest the 256 x 256 eight-wave tile.
+hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, void* c, int64_t M,
+                             int64_t N, int64_t K, bool out_f32, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmParams p{};
+  p.a = (const uint8_t*)x; p.a_s = nullptr; p.b = (const uint8_t*)w; p.b_s = w_s; p.c = c;
+  p.offsets = nullptr; p.rows = (int)M; p.N = (int)N; p.K = (int)K; p.E = 0;
+  if (M <= 32) return run_w8a16<32, 64, 32, 16, 4, 6, 2>(p, out_f32, stream);
+  if (M <= 64) return run_w8a16<64, 64, 64, 16, 4, 6, 2>(p, out_f32, stream);
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles < device_cus()) return run_w8a16<128, 128, 64, 64, 4, 4, 1>(p, out_f32, stream);
+  return run_w8a16<256, 256, 128, 64, 8, 3, 1>(p, out_f32, stream);
 }
 
 }  // namespace fp8bs

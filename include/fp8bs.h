@@ -155,6 +155,24 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
                    int out_dtype, void* stream);
 
 /*
+ * w8a16_gemm -- the BF16 path of the linear (Admin guide 6.3, gemm_impl
+ * "bf16"): C = x . weight_dequant(w, w_s)^T with the weight dequantised as
+ * fp8bs_weight_dequant does (bf16(RN32(decode(q) * s))) but never stored:
+ * the kernel dequantises in registers and multiplies with bf16 MFMA,
+ * accumulating in float32.
+ *
+ *   x_bf16   in   bf16 [M, K]
+ *   w_e4m3   in   e4m3 [N, K] (nn.Linear out x in)
+ *   w_s      in   float32 [ceil(N/128), K/128]
+ *   c        out  [M, N] bf16 or float32 (out_dtype)
+ *   M, N >= 0 (either 0 = no-op), K >= 128 with K % 128 == 0;
+ *   (M + 256) * 2K < 2^32 and (N + 256) * K < 2^32.
+ * x, w and c 16-byte aligned, w_s 4-byte aligned; c must not overlap an input.
+ */
+int fp8bs_w8a16_gemm(const void* x_bf16, const void* w_e4m3, const float* w_s, void* c, int64_t M,
+                     int64_t N, int64_t K, int out_dtype, void* stream);
+
+/*
  * MoE dispatch and combine -- the steps around fp8bs_moe_gemm in the expert
  * loop of the Admin guide (6.4; the annotated forward pass in 8.4): hit
  * counts of the routed expert ids, each expert's (token, slot) pairs in token

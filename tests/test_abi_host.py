@@ -111,6 +111,19 @@ def test_moe_gemm_validation(L):
     assert m(None, None, None, None, None, None, 8, 0, 4, 128, 0, None) == OK
 
 
+def test_w8a16_gemm_validation(L):
+    g = L.fp8bs_w8a16_gemm
+    assert g(P0, P1, P2, P3, 4, 4, 100, 0, None) == SHAPE        # K % 128
+    assert g(P0, P1, P2, P3, -1, 4, 128, 0, None) == SHAPE
+    assert g(P0, P1, P2, P3, 4, 4, 128, 3, None) == ENUM
+    assert g(P0, None, P2, P3, 4, 4, 128, 0, None) == NULL
+    assert g(P0, P1, P2 + 2, P3, 4, 4, 128, 0, None) == ALIGN
+    assert g(P0, P1, P2, P3 + 8, 4, 4, 128, 0, None) == ALIGN
+    assert g(P0, P1, P2, P0, 4, 4, 128, 0, None) == ALIAS        # C over x
+    assert g(None, None, None, None, 0, 4, 128, 0, None) == OK
+    assert g(P0, P1, P2, P3, 1 << 24, 4, 128, 0, None) == SHAPE  # (M + 256) * 2K >= 2^32
+
+
 def test_moe_route_validation(L):
     r = L.fp8bs_moe_route
     ws = L.fp8bs_moe_route_workspace_size
