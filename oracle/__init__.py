@@ -66,6 +66,7 @@ def _load():
     lib.orc_block_scale.restype = ctypes.c_float
     lib.orc_act_quant.argtypes = [P, I64, I64, ctypes.c_int, P, P]
     lib.orc_weight_quant.argtypes = [P, I64, I64, P, P]
+    lib.orc_weight_quant_fmt.argtypes = [P, I64, I64, ctypes.c_int, P, P]
     lib.orc_weight_dequant.argtypes = [P, P, I64, I64, P]
     lib.orc_gemm.argtypes = [P, P, P, P, I64, I64, I64, P]
     lib.orc_gemm_points.argtypes = [P, P, P, P, I64, P, P, I64, P]
@@ -149,15 +150,17 @@ def act_quant(x_bf16_bits: np.ndarray, fmt: int = FMT_FP32):
     return q, s
 
 
-def weight_quant(w_bf16_bits: np.ndarray):
-    """128x128 block quantisation of a bf16 weight ``uint16 [N, K]`` (any N, K).
+def weight_quant(w_bf16_bits: np.ndarray, fmt: int = FMT_FP32):
+    """128x128 block quantisation of a bf16 weight ``uint16 [N, K]`` (any N, K)
+    with act_quant's rule per block (fmt FMT_UE8M0: power-of-two scales, a
+    harness option for the ue8m0 fast path).
 
     Returns (q uint8 [N, K], s float32 [ceil(N/128), ceil(K/128)])."""
     w = _c(w_bf16_bits, np.uint16)
     N, K = w.shape
     q = np.empty((N, K), dtype=np.uint8)
     s = np.empty(((N + BLOCK - 1) // BLOCK, (K + BLOCK - 1) // BLOCK), dtype=np.float32)
-    _load().orc_weight_quant(_ptr(w), N, K, _ptr(q), _ptr(s))
+    _load().orc_weight_quant_fmt(_ptr(w), N, K, int(fmt), _ptr(q), _ptr(s))
     return q, s
 
 

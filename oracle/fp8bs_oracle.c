@@ -201,7 +201,11 @@ void orc_act_quant(const uint16_t* x, int64_t M, int64_t K, int fmt, uint8_t* q,
 /* ------------------------------------------------------------------------ */
 
 /* w: bf16 [N, K]; q: e4m3 [N, K]; s: binary32 [ceil(N/128), ceil(K/128)]. */
-void orc_weight_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s) {
+/* fmt selects the scale rule as for act_quant: float32 or rounded up to a
+ * power of two (ue8m0).  The pages round only activation scales; power-of-two
+ * weight scales are a harness option for the ue8m0 fast path, where both
+ * operands carry power-of-two scales. */
+void orc_weight_quant_fmt(const uint16_t* w, int64_t N, int64_t K, int fmt, uint8_t* q, float* s) {
     mag_init();
     int64_t nbn = (N + ORC_BLOCK - 1) / ORC_BLOCK, nbk = (K + ORC_BLOCK - 1) / ORC_BLOCK;
 #pragma omp parallel for collapse(2) schedule(static)
@@ -215,13 +219,17 @@ void orc_weight_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float
                     float v = fabsf(orc_bf16_to_f32(w[n * K + k]));
                     if (v > amax) amax = v;
                 }
-            float sc = orc_block_scale(amax, ORC_FMT_FP32);
+            float sc = orc_block_scale(amax, fmt);
             s[bn * nbk + bk] = sc;
             for (int64_t n = n0; n < n1; ++n)
                 for (int64_t k = k0; k < k1; ++k)
                     q[n * K + k] = quant_one(orc_bf16_to_f32(w[n * K + k]), sc);
         }
     }
+}
+
+void orc_weight_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s) {
+    orc_weight_quant_fmt(w, N, K, ORC_FMT_FP32, q, s);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -607,3 +607,36 @@ def test_w8a16_points_equal_full(orc):
     full = orc.w8a16_gemm(x, q, s)
     r, c = rng.integers(0, M, 30), rng.integers(0, N, 30)
     assert np.array_equal(orc.w8a16_gemm_points(x, q, s, r, c), full[r, c])
+
+
+# ------------------------------------------------ power-of-two weight scales
+
+def test_weight_quant_ue8m0_single_row_equals_act_quant(orc):
+    """A one-row weight has 1 x 128 blocks, so its ue8m0 block quantisation
+    is act_quant's ue8m0 rule (pinned above) on the same row."""
+    w = inputs.bf16_bits(inputs.normal_bf16((1, 640), 0.02, 81, outlier_frac=0.02, outlier_mult=50.0))
+    q, s = orc.weight_quant(w, orc.FMT_UE8M0)
+    qa, sa = orc.act_quant(w, orc.FMT_UE8M0)
+    assert np.array_equal(q, qa) and np.array_equal(s.view(np.uint32), sa.view(np.uint32))
+
+
+def test_weight_quant_ue8m0_closed_forms(orc):
+    """Every scale is a power of two, at least the float32 scale and less
+    than twice it; the codes equal the plain e4m3 rounding of w / s (exact
+    division by a power of two), checked with torch's cast; the largest code
+    magnitude of a block with amax above the floor lies in (224, 448]."""
+    w_t = inputs.normal_bf16((300, 260), 0.02, 82)
+    w = inputs.bf16_bits(w_t)
+    q, s = orc.weight_quant(w, orc.FMT_UE8M0)
+    _, s32 = orc.weight_quant(w, orc.FMT_FP32)
+    m, e = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)
+    assert np.all(s >= s32) and np.all(s < 2 * s32)
+    sf = torch.from_numpy(np.repeat(np.repeat(s, 128, 0), 128, 1)[:300, :260])
+    ref = (w_t.float() / sf).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    dec = np.abs(orc.e4m3_decode_array(q))
+    for bn in range(3):
+        for bk in range(3):
+            blk = dec[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128]
+            assert 224 < blk.max() <= 448
