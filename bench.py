@@ -326,6 +326,31 @@ def bench_w8a16(steps, warmup, dev, out):
         del ws, x, y
 
 
+def bench_ue8m0(steps, warmup, dev, out):
+    """The ue8m0 fast path (power-of-two scales applied by the scaled MFMA) on
+    the prefill GEMM and on the two GEMM shapes of the ue8m0 workload."""
+    for (M, N, K, cfg, tx, tw) in [(4096, 18432, 7168, 3, 0, 1), (1024, 1536, 7168, 5, 2, 3),
+                                   (1024, 16384, 512, 5, 4, 5)]:
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, tx), dev)
+        xq, xs = fp8bs.act_quant(x, "ue8m0")
+        del x
+        nb = gemm_bytes(M, N, K)
+        copies = 1 if M == 4096 else n_copies(nb)
+        ws = []
+        for c in range(copies):
+            w = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(cfg, tw) + 100 * c, dev)
+            ws.append(fp8bs.weight_quant(w, "ue8m0"))
+            del w
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, ws[c][0], ws[c][1], y, ue8m0=True), copies,
+                   steps, warmup)
+        ai = 2 * M * N * K / nb
+        out[f"gemm_ue8m0_scaled_mfma_{M}x{N}x{K}"] = row_result(
+            f"gemm ue8m0 {M}x{N}x{K}", us, 2 * M * N * K, nb, "mfma" if ai > 629 else "hbm",
+            {"copies": copies})
+        del ws, xq, xs, y
+
+
 def cpu_baseline(x_dev, w_dev, budget_s):
     """The oracle on a row sample of the prefill linear: act_quant of the
     sampled rows of x, then all N outputs of each sampled row in binary64, with
@@ -359,7 +384,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
-                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,down")
+                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -396,7 +421,8 @@ def main():
                                                         act_quant_bytes(M, K), "hbm")
     rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
                                                          gemm_bytes(M, N, K), "mfma")
-    sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "w8a16", "down"]) if args.rows == "all" else (
+    sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "w8a16", "ue8m0",
+             "down"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
@@ -418,6 +444,8 @@ def main():
         bench_moe_dispatch(args.steps, args.warmup, dev, rows)
     if "w8a16" in sel:
         bench_w8a16(args.steps, args.warmup, dev, rows)
+    if "ue8m0" in sel:
+        bench_ue8m0(args.steps, args.warmup, dev, rows)
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6

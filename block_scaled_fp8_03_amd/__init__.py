@@ -29,8 +29,8 @@ __all__ = [
     "SCALE_FP32", "SCALE_UE8M0", "OUT_BF16", "OUT_F32", "Fp8bsError", "library_path", "lib",
     "fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
     "fp8bs_moe_gemm", "fp8bs_w8a16_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter",
-    "fp8bs_moe_combine", "w8a16_gemm",
-    "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm", "linear", "moe_route",
+    "fp8bs_moe_combine", "w8a16_gemm", "fp8bs_gemm_ue8m0", "fp8bs_weight_quant_ue8m0",
+    "fp8_gemm_ue8m0", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm", "linear", "moe_route",
     "moe_quant_scatter", "moe_combine",
 ]
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     L.fp8bs_moe_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, P]
     L.fp8bs_w8a16_gemm.argtypes = [P, P, P, P, I64, I64, I64, I, P]
+    L.fp8bs_gemm_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
+    L.fp8bs_weight_quant_ue8m0.argtypes = [P, P, P, I64, I64, P]
     L.fp8bs_moe_route_workspace_size.argtypes = [I64, I64, I64]
     L.fp8bs_moe_route_workspace_size.restype = I64
     L.fp8bs_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
@@ -79,7 +81,7 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_moe_combine.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     for fn in ("fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
                "fp8bs_moe_gemm", "fp8bs_w8a16_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter",
-               "fp8bs_moe_combine"):
+               "fp8bs_moe_combine", "fp8bs_gemm_ue8m0", "fp8bs_weight_quant_ue8m0"):
         getattr(L, fn).restype = I
     _lib = L
     return L
@@ -141,13 +143,15 @@ def fp8bs_act_quant(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, scale_fmt
           _need(s, (torch.float32,), "s"), M, K, _fmt(scale_fmt), _stream(x))
 
 
-def fp8bs_weight_quant(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor) -> None:
-    """w bf16 [N, K] -> q e4m3 [N, K], s float32 [ceil(N/128), ceil(K/128)]."""
+def fp8bs_weight_quant(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, scale_fmt=SCALE_FP32) -> None:
+    """w bf16 [N, K] -> q e4m3 [N, K], s float32 [ceil(N/128), ceil(K/128)]
+    (scale_fmt "ue8m0": power-of-two block scales)."""
     N, K = w.shape
     if tuple(q.shape) != (N, K) or tuple(s.shape) != (-(-N // BLOCK), -(-K // BLOCK)):
         raise ValueError("q must be [N, K] and s [ceil(N/128), ceil(K/128)]")
-    _call("fp8bs_weight_quant", _need(w, (torch.bfloat16,), "w"), _need(q, _F8, "q"),
-          _need(s, (torch.float32,), "s"), N, K, _stream(w))
+    fn = "fp8bs_weight_quant_ue8m0" if _fmt(scale_fmt) == SCALE_UE8M0 else "fp8bs_weight_quant"
+    _call(fn, _need(w, (torch.bfloat16,), "w"), _need(q, _F8, "q"), _need(s, (torch.float32,), "s"),
+          N, K, _stream(w))
 
 
 def fp8bs_weight_dequant(w: torch.Tensor, s: torch.Tensor, y: torch.Tensor) -> None:
@@ -160,8 +164,9 @@ def fp8bs_weight_dequant(w: torch.Tensor, s: torch.Tensor, y: torch.Tensor) -> N
 
 
 def fp8bs_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
-               c: torch.Tensor) -> None:
-    """C [M, N] (bf16 or float32, by c.dtype) = block-scaled A [M, K] . B [N, K]^T."""
+               c: torch.Tensor, ue8m0: bool = False) -> None:
+    """C [M, N] (bf16 or float32, by c.dtype) = block-scaled A [M, K] . B [N, K]^T.
+    ue8m0=True calls fp8bs_gemm_ue8m0 (all scales must be powers of two)."""
     M, K = a.shape
     N, K2 = b.shape
     if K != K2 or K % BLOCK:
@@ -169,7 +174,8 @@ def fp8bs_gemm(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.T
     if (tuple(a_s.shape) != (M, K // BLOCK) or tuple(b_s.shape) != (-(-N // BLOCK), K // BLOCK)
             or tuple(c.shape) != (M, N)):
         raise ValueError("scale or output shape mismatch")
-    _call("fp8bs_gemm", _need(a, _F8, "a"), _need(a_s, (torch.float32,), "a_s"),
+    _call("fp8bs_gemm_ue8m0" if ue8m0 else "fp8bs_gemm", _need(a, _F8, "a"),
+          _need(a_s, (torch.float32,), "a_s"),
           _need(b, _F8, "b"), _need(b_s, (torch.float32,), "b_s"),
           _need(c, (torch.bfloat16, torch.float32), "c"), M, N, K, _out_code(c), _stream(a))
 
@@ -261,11 +267,11 @@ def act_quant(x: torch.Tensor, scale_fmt="fp32"):
     return q.view(x.shape), s.view(*x.shape[:-1], K // BLOCK)
 
 
-def weight_quant(w: torch.Tensor):
+def weight_quant(w: torch.Tensor, scale_fmt="fp32"):
     N, K = w.shape
     q = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
     s = torch.empty((-(-N // BLOCK), -(-K // BLOCK)), dtype=torch.float32, device=w.device)
-    fp8bs_weight_quant(w, q, s)
+    fp8bs_weight_quant(w, q, s, scale_fmt)
     return q, s
 
 
@@ -278,6 +284,13 @@ def weight_dequant(w: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
 def fp8_gemm(a, a_s, b, b_s, out_dtype=torch.bfloat16) -> torch.Tensor:
     c = torch.empty((a.shape[0], b.shape[0]), dtype=out_dtype, device=a.device)
     fp8bs_gemm(a, a_s, b, b_s, c)
+    return c
+
+
+def fp8_gemm_ue8m0(a, a_s, b, b_s, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """fp8_gemm for power-of-two scales, the scales applied by the MFMA."""
+    c = torch.empty((a.shape[0], b.shape[0]), dtype=out_dtype, device=a.device)
+    fp8bs_gemm(a, a_s, b, b_s, c, ue8m0=True)
     return c
 
 

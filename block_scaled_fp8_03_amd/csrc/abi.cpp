@@ -71,8 +71,8 @@ int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64
                                            scale_fmt == FP8BS_SCALE_UE8M0, (hipStream_t)stream));
 }
 
-int fp8bs_weight_quant(const void* w_bf16, void* q_e4m3, float* s, int64_t N, int64_t K,
-                       void* stream) {
+static int weight_quant_entry(bool ue8m0, const void* w_bf16, void* q_e4m3, float* s, int64_t N,
+                              int64_t K, void* stream) {
   if (N < 0 || K < 0) return FP8BS_ERR_SHAPE;
   const int64_t n = mul(N, K);
   if (n < 0 || mul(n, 2) < 0 || cdiv(N, 128) > 65535 || cdiv(K, 128) > kLimitInt)
@@ -84,7 +84,17 @@ int fp8bs_weight_quant(const void* w_bf16, void* q_e4m3, float* s, int64_t N, in
   if (overlap(q_e4m3, n, w_bf16, 2 * n) || overlap(s, 4 * ns, w_bf16, 2 * n) ||
       overlap(q_e4m3, n, s, 4 * ns))
     return FP8BS_ERR_ALIAS;
-  return status_of(fp8bs::launch_weight_quant(w_bf16, q_e4m3, s, N, K, (hipStream_t)stream));
+  return status_of(fp8bs::launch_weight_quant(w_bf16, q_e4m3, s, N, K, ue8m0, (hipStream_t)stream));
+}
+
+int fp8bs_weight_quant(const void* w_bf16, void* q_e4m3, float* s, int64_t N, int64_t K,
+                       void* stream) {
+  return weight_quant_entry(false, w_bf16, q_e4m3, s, N, K, stream);
+}
+
+int fp8bs_weight_quant_ue8m0(const void* w_bf16, void* q_e4m3, float* s, int64_t N, int64_t K,
+                             void* stream) {
+  return weight_quant_entry(true, w_bf16, q_e4m3, s, N, K, stream);
 }
 
 int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64_t N, int64_t K,
@@ -100,8 +110,8 @@ int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64
   return status_of(fp8bs::launch_weight_dequant(w_e4m3, s, y_bf16, N, K, (hipStream_t)stream));
 }
 
-int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
-               int64_t M, int64_t N, int64_t K, int out_dtype, void* stream) {
+static int gemm_entry(bool ue8m0, const void* a, const float* a_s, const void* b, const float* b_s,
+                      void* c, int64_t M, int64_t N, int64_t K, int out_dtype, void* stream) {
   if (M < 0 || N < 0 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ENUM;
   if (M > kLimitInt || N > kLimitInt || K > kLimitInt) return FP8BS_ERR_SHAPE;
@@ -119,8 +129,19 @@ int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
   if (overlap(c, cb, a, na) || overlap(c, cb, b, nb) || overlap(c, cb, a_s, nas) ||
       overlap(c, cb, b_s, nbs))
     return FP8BS_ERR_ALIAS;
-  return status_of(fp8bs::launch_gemm(a, a_s, b, b_s, c, M, N, K, out_dtype == FP8BS_OUT_F32,
-                                      (hipStream_t)stream));
+  const bool f32 = out_dtype == FP8BS_OUT_F32;
+  return status_of(ue8m0 ? fp8bs::launch_gemm_ue8m0(a, a_s, b, b_s, c, M, N, K, f32, (hipStream_t)stream)
+                         : fp8bs::launch_gemm(a, a_s, b, b_s, c, M, N, K, f32, (hipStream_t)stream));
+}
+
+int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+               int64_t M, int64_t N, int64_t K, int out_dtype, void* stream) {
+  return gemm_entry(false, a, a_s, b, b_s, c, M, N, K, out_dtype, stream);
+}
+
+int fp8bs_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+                     int64_t M, int64_t N, int64_t K, int out_dtype, void* stream) {
+  return gemm_entry(true, a, a_s, b, b_s, c, M, N, K, out_dtype, stream);
 }
 
 int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,

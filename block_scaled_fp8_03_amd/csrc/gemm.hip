@@ -162,8 +162,12 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
 // Stages that start no chunk issue an out-of-range dummy load (no memory
 // traffic) when ST > 2 so that every stage has the same number of DMA ops.
 // OCC workgroups share a CU (register budget set for OCC * NW / 4 waves per SIMD).
+// E8: every a_s and b_s value is a power of two; the MFMA applies them itself
+// (v_mfma_scale_f32_16x16x128_f8f6f4 with each lane's E8M0 exponent: the
+// weight block's for the weight operand, its activation row's for the other)
+// and accumulates straight into the fp32 accumulators -- no VALU fold.
 template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool MOE,
-          int OCC>
+          int OCC, bool E8 = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))
 gemm_tile_kernel(GemmParams p) {
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
@@ -342,6 +346,15 @@ gemm_tile_kernel(GemmParams p) {
     for (int t = 0; t < MT; ++t) {
       const int ml = wm * WM + 16 * t + r16;
       const v8i af = lds_frag<SW>(at, ml, g);
+      if (E8) {
+        // E8M0 exponents: the biased exponent field of each power-of-two scale
+        const int ea = (int)(f32_bits(ast[ml * ASC + as_col]) >> 23);
+        const int eb = (int)(f32_bits(bsv) >> 23);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[j][t], 0, 0, 0, eb, 0, ea);
+        continue;
+      }
       const float sc = ast[ml * ASC + as_col] * bsv;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -773,23 +786,23 @@ w8a16_tile_kernel(GemmParams p) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool MOE, int OCC>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool MOE, int OCC, bool E8>
 void launch_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   if (out_f32)
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, MOE, OCC><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, MOE, OCC, E8><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
   else
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, MOE, OCC><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, MOE, OCC, E8><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
 }
 
 // Chunked a_s loads (16 bytes per lane) need every row of a_s to start on a
 // 16-byte boundary.
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE, int OCC = 1>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE, int OCC = 1, bool E8 = false>
 hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   const bool chunked = (p.K / 128) % 4 == 0 && ((uintptr_t)p.a_s & 15) == 0;
   if (chunked)
-    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, MOE, OCC>(p, out_f32, grid, stream);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, MOE, OCC, E8>(p, out_f32, grid, stream);
   else
-    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, MOE, OCC>(p, out_f32, grid, stream);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, MOE, OCC, E8>(p, out_f32, grid, stream);
   return hipGetLastError();
 }
 
@@ -823,8 +836,9 @@ hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
-                       int64_t M, int64_t N, int64_t K, bool out_f32, hipStream_t stream) {
+template <bool E8>
+hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+                      int64_t M, int64_t N, int64_t K, bool out_f32, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmParams p{};
   p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
@@ -847,15 +861,28 @@ hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const flo
     if (tiles(128, 128) >= cus / 2) {
       p.num_m = (int)((M + 127) / 128);
       p.num_n = (int)((N + 127) / 128);
-      return run_tile<128, 128, 64, 64, 3, 4, 2, false>(p, out_f32, p.num_m * p.num_n, stream);
+      return run_tile<128, 128, 64, 64, 3, 4, 2, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
     }
     p.num_m = (int)((M + 63) / 64);
     p.num_n = (int)((N + 63) / 64);
-    return run_tile<64, 64, 32, 32, 3, 4, 2, false, 2>(p, out_f32, p.num_m * p.num_n, stream);
+    return run_tile<64, 64, 32, 32, 3, 4, 2, false, 2, E8>(p, out_f32, p.num_m * p.num_n, stream);
   }
   p.num_m = (int)((M + BM - 1) / BM);
   p.num_n = (int)((N + BN - 1) / BN);
-  return run_tile<FP8BS_TILE_CFG, false>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
+}
+
+hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+                       int64_t M, int64_t N, int64_t K, bool out_f32, hipStream_t stream) {
+  return dense_gemm<false>(a, a_s, b, b_s, c, M, N, K, out_f32, stream);
+}
+
+// The ue8m0 fast path: same tiles, scales applied by the MFMA (decode-sized M
+// keeps the decode kernel, which handles any scales).
+hipError_t launch_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s,
+                             void* c, int64_t M, int64_t N, int64_t K, bool out_f32,
+                             hipStream_t stream) {
+  return dense_gemm<true>(a, a_s, b, b_s, c, M, N, K, out_f32, stream);
 }
 
 hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,

@@ -10,7 +10,7 @@ namespace fp8bs {
 
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
                             hipStream_t stream);
-hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K,
+hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K, bool ue8m0,
                                hipStream_t stream);
 hipError_t launch_weight_dequant(const void* w, const float* s, void* y, int64_t N, int64_t K,
                                  hipStream_t stream);
@@ -20,6 +20,9 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
                            const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N,
                            int64_t K, bool out_f32, hipStream_t stream);
 
+hipError_t launch_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s,
+                             void* c, int64_t M, int64_t N, int64_t K, bool out_f32,
+                             hipStream_t stream);
 hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, void* c, int64_t M,
                              int64_t N, int64_t K, bool out_f32, hipStream_t stream);
 hipError_t launch_moe_quant_scatter(const void* x, const int32_t* row_of, void* q, float* s,

@@ -127,6 +127,9 @@ __device__ __forceinline__ float block_amax_256(uint32_t m, uint32_t* red) {
   return bits_f32(m);
 }
 
+// UE8M0: power-of-two block scales (act_quant's ue8m0 rule per 128 x 128
+// block), a harness option for the ue8m0 fast path of the GEMM.
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void weight_quant_kernel(const uint16_t* __restrict__ w,
                                                            uint8_t* __restrict__ q,
                                                            float* __restrict__ s, int64_t N,
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const uint16_t* __res
       for (int j = 0; j < 4; ++j)
         m = max(m, max(f32_bits(bf16_lo(ws[j])) & 0x7FFFFFFFu, f32_bits(bf16_hi(ws[j])) & 0x7FFFFFFFu));
     }
-    const float sc = block_scale<false>(block_amax_256(m, red));
+    const float sc = block_scale<UE8M0>(block_amax_256(m, red));
     const float r = __fdiv_rn(1.0f, sc);
     uint4* dst = (uint4*)(q + n * K + k0);
 #pragma unroll
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const uint16_t* __res
     if (n < N)
       for (int j = 0; j < 64; ++j)
         if (k0 + j < K) m = max(m, f32_bits(bf16_lo(w[n * K + k0 + j])) & 0x7FFFFFFFu);
-    const float sc = block_scale<false>(block_amax_256(m, red));
+    const float sc = block_scale<UE8M0>(block_amax_256(m, red));
     const float r = __fdiv_rn(1.0f, sc);
     if (n < N)
       for (int j = 0; j < 64; j += 4) {
@@ -191,12 +194,16 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const uint16_t* __res
   }
 }
 
-hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K,
+hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K, bool ue8m0,
                                hipStream_t stream) {
   if (N == 0 || K == 0) return hipSuccess;
   const int64_t nbn = (N + kBlock - 1) / kBlock, nbk = (K + kBlock - 1) / kBlock;
-  weight_quant_kernel<<<dim3((unsigned)nbk, (unsigned)nbn), dim3(256), 0, stream>>>(
-      (const uint16_t*)w, (uint8_t*)q, s, N, K);
+  if (ue8m0)
+    weight_quant_kernel<true><<<dim3((unsigned)nbk, (unsigned)nbn), dim3(256), 0, stream>>>(
+        (const uint16_t*)w, (uint8_t*)q, s, N, K);
+  else
+    weight_quant_kernel<false><<<dim3((unsigned)nbk, (unsigned)nbn), dim3(256), 0, stream>>>(
+        (const uint16_t*)w, (uint8_t*)q, s, N, K);
   return hipGetLastError();
 }
 

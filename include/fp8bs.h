@@ -155,6 +155,29 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
                    int out_dtype, void* stream);
 
 /*
+ * gemm_ue8m0 -- fp8bs_gemm for operands whose scales are all powers of two
+ * (act_quant with FP8BS_SCALE_UE8M0 and fp8bs_weight_quant_ue8m0), the ue8m0
+ * variant of the pages (User guide FAQ; Admin guide 8.5.1).  The result is the
+ * same sum; the kernel passes each scale's exponent to the MFMA
+ * (v_mfma_scale_f32_16x16x128_f8f6f4, E8M0 scales) instead of folding the
+ * scales in with VALU instructions.  Arguments as fp8bs_gemm.
+ * PRECONDITION (not checked on the host: the scales live on the device):
+ * every a_s and b_s value is 2^k with -126 <= k <= 127; only the exponent
+ * field is read, so other values give wrong results, not faults.
+ */
+int fp8bs_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
+                     int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
+
+/*
+ * weight_quant_ue8m0 -- fp8bs_weight_quant with each block scale rounded up
+ * to a power of two (act_quant's ue8m0 rule on 128 x 128 blocks); a harness
+ * option: the pages round only activation scales.  Arguments as
+ * fp8bs_weight_quant.
+ */
+int fp8bs_weight_quant_ue8m0(const void* w_bf16, void* q_e4m3, float* s, int64_t N, int64_t K,
+                             void* stream);
+
+/*
  * w8a16_gemm -- the BF16 path of the linear (Admin guide 6.3, gemm_impl
  * "bf16"): C = x . weight_dequant(w, w_s)^T with the weight dequantised as
  * fp8bs_weight_dequant does (bf16(RN32(decode(q) * s))) but never stored:

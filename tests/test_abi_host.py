@@ -70,11 +70,12 @@ def test_act_quant_validation(L):
 
 
 def test_weight_quant_and_dequant_validation(L):
-    assert L.fp8bs_weight_quant(P0, P1, P2, -3, 5, None) == SHAPE
-    assert L.fp8bs_weight_quant(None, P1, P2, 3, 5, None) == NULL
-    assert L.fp8bs_weight_quant(P0 + 2, P1, P2, 3, 5, None) == ALIGN
-    assert L.fp8bs_weight_quant(P0, P0, P2, 3, 5, None) == ALIAS
-    assert L.fp8bs_weight_quant(None, None, None, 0, 5, None) == OK
+    for wq in (L.fp8bs_weight_quant, L.fp8bs_weight_quant_ue8m0):
+        assert wq(P0, P1, P2, -3, 5, None) == SHAPE
+        assert wq(None, P1, P2, 3, 5, None) == NULL
+        assert wq(P0 + 2, P1, P2, 3, 5, None) == ALIGN
+        assert wq(P0, P0, P2, 3, 5, None) == ALIAS
+        assert wq(None, None, None, 0, 5, None) == OK
     assert L.fp8bs_weight_dequant(P0, P1, P2, 3, -5, None) == SHAPE
     assert L.fp8bs_weight_dequant(P0, None, P2, 3, 5, None) == NULL
     assert L.fp8bs_weight_dequant(P0, P1, P2 + 8, 3, 5, None) == ALIGN
@@ -82,8 +83,9 @@ def test_weight_quant_and_dequant_validation(L):
     assert L.fp8bs_weight_dequant(None, None, None, 7, 0, None) == OK
 
 
-def test_gemm_validation(L):
-    g = L.fp8bs_gemm
+@pytest.mark.parametrize("name", ["fp8bs_gemm", "fp8bs_gemm_ue8m0"])
+def test_gemm_validation(L, name):
+    g = getattr(L, name)
     assert g(P0, P1, P2, P3, P4, 4, 4, 100, 0, None) == SHAPE        # K % 128
     assert g(P0, P1, P2, P3, P4, 4, 4, 0, 0, None) == SHAPE          # K = 0
     assert g(P0, P1, P2, P3, P4, -4, 4, 128, 0, None) == SHAPE

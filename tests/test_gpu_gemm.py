@@ -60,6 +60,22 @@ def test_gemm_tile_configs(M, N, K):
     assert_close(run_gemm(a, a_s, b, b_s, torch.bfloat16), ref, f"gemm[{M}x{N}x{K}] bf16")
 
 
+@pytest.mark.parametrize("M,N,K", [(257, 300, 1536), (1000, 2100, 1536)])
+def test_gemm_tile_outliers(M, N, K):
+    """The tile path on activations with 1% x50 outliers.  One dominant product
+    costs the other 127 of its FP8-MFMA block low bits (measured up to 2^-13.6
+    of the sum of |products|), so the bar carries the hardware term 2^-11 *
+    (oracle GEMM of the magnitudes); all but a few elements in 10^4 still meet
+    the plain bar."""
+    a, a_s, b, b_s = rand_operands(M, N, K, 5500 + M + N + K, outliers=True)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    mag = oracle.gemm(a & 0x7F, a_s, b & 0x7F, b_s)
+    got = run_gemm(a, a_s, b, b_s, torch.float32).astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-2 * np.abs(ref) + 1e-3 + 2.0 ** -11 * mag), "hardware-term bar"
+    assert (err > 1e-2 * np.abs(ref) + 1e-3).mean() < 1e-3, "plain bar"
+
+
 def test_gemm_unaligned_scales():
     """a_s starting 4 bytes past a 16-byte boundary: the kernel must then
     read the activation scales one float at a time (K/128 is a multiple of 4
