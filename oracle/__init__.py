@@ -74,6 +74,8 @@ def _load():
     lib.orc_moe_gemm_points.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, I64, P]
     lib.orc_w8a16_gemm.argtypes = [P, P, P, I64, I64, I64, P]
     lib.orc_w8a16_gemm_points.argtypes = [P, P, P, I64, I64, P, P, I64, P]
+    lib.orc_mla_absorb.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, I64, I64, P]
+    lib.orc_mla_absorb_points.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, I64, P, P, P, I64, P]
     lib.orc_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.orc_moe_route.restype = I64
     lib.orc_moe_quant_scatter.argtypes = [P, I64, I64, ctypes.c_int, P, I64, I64, P, P]
@@ -279,6 +281,53 @@ def w8a16_gemm_points(x_bf16_bits, q, s, rows, cols) -> np.ndarray:
     out = np.empty(rows.shape, dtype=np.float64)
     _load().orc_w8a16_gemm_points(_ptr(x), _ptr(q), _ptr(s), N, K, _ptr(rows), _ptr(cols), rows.size,
                                   _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------------ MLA absorb
+
+MLA_KEY, MLA_VALUE = 0, 1
+
+
+def _mla_check(side, inp, w, s, dn, dv):
+    inp = _c(inp, np.uint16)
+    w = _c(w, np.uint8)
+    s = _c(s, np.float32)
+    T, H, width = inp.shape
+    rows, R = w.shape
+    if rows != H * (dn + dv) or width != (dn if side == MLA_KEY else R):
+        raise ValueError("wkv_b must be [H*(dn+dv), R]; q [T, H, dn] or x [T, H, R]")
+    if s.shape != (-(-rows // BLOCK), -(-R // BLOCK)):
+        raise ValueError("scale shape")
+    return inp, w, s, T, H, R
+
+
+def mla_absorb(side: int, inp_bf16_bits: np.ndarray, w: np.ndarray, s: np.ndarray, dn: int,
+               dv: int) -> np.ndarray:
+    """MLA absorb with an FP8 wkv_b (Admin guide 8.3 steps 5 and 7, the weight
+    dequantised as weight_dequant does), in binary64.
+
+    side MLA_KEY:   q bf16 bits [T, H, dn] -> [T, H, R],
+                    out[t,h,c] = sum_d q[t,h,d] Wd[h(dn+dv)+d, c]
+    side MLA_VALUE: x bf16 bits [T, H, R] -> [T, H, dv],
+                    out[t,h,d] = sum_c x[t,h,c] Wd[h(dn+dv)+dn+d, c]"""
+    inp, w, s, T, H, R = _mla_check(side, inp_bf16_bits, w, s, dn, dv)
+    ncol = R if side == MLA_KEY else dv
+    out = np.empty((T, H, ncol), dtype=np.float64)
+    _load().orc_mla_absorb(int(side), _ptr(inp), _ptr(w), _ptr(s), T, H, dn, dv, R, _ptr(out))
+    return out
+
+
+def mla_absorb_points(side: int, inp_bf16_bits, w, s, dn, dv, ts, hs, cols) -> np.ndarray:
+    """mla_absorb at the points (ts[i], hs[i], cols[i])."""
+    inp, w, s, T, H, R = _mla_check(side, inp_bf16_bits, w, s, dn, dv)
+    ts, hs, cols = (_c(np.asarray(a, dtype=np.int64), np.int64) for a in (ts, hs, cols))
+    ncol = R if side == MLA_KEY else dv
+    assert ts.size == 0 or (0 <= ts.min() and ts.max() < T and 0 <= hs.min() and hs.max() < H
+                            and 0 <= cols.min() and cols.max() < ncol)
+    out = np.empty(ts.shape, dtype=np.float64)
+    _load().orc_mla_absorb_points(int(side), _ptr(inp), _ptr(w), _ptr(s), H, dn, dv, R, _ptr(ts),
+                                  _ptr(hs), _ptr(cols), ts.size, _ptr(out))
     return out
 
 

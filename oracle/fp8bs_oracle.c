@@ -367,6 +367,64 @@ void orc_w8a16_gemm_points(const uint16_t* x, const uint8_t* q, const float* s, 
 }
 
 /* ------------------------------------------------------------------------ */
+/* MLA "absorb" with an FP8 wkv_b (Admin guide 8.3, steps 5 and 7; the FP8   */
+/* weight is dequantised by weight_dequant (8.5.2), then used in the two      */
+/* einsums).  wkv_b [H*(dn+dv), R] viewed as [H, dn+dv, R]: the first dn     */
+/* rows of head h absorb q_nope into the latent space, the last dv rows turn  */
+/* the attention-weighted latent into the head's values:                     */
+/*   key side   out[t,h,c] = sum_{d<dn} q[t,h,d] * Wd[h(dn+dv) + d, c]        */
+/*   value side out[t,h,d] = sum_{c<R}  x[t,h,c] * Wd[h(dn+dv) + dn + d, c]   */
+/* q [T,H,dn] and x [T,H,R] are bf16, products are exact in binary64 and the  */
+/* sums run in binary64 in index order.                                      */
+/* ------------------------------------------------------------------------ */
+static double mla_point(int side, const uint16_t* in, const uint16_t* wd, int64_t H, int64_t dn,
+                        int64_t dv, int64_t R, int64_t t, int64_t h, int64_t col) {
+    double acc = 0.0;
+    if (side == 0) {            /* key side: col = c, sum over d */
+        for (int64_t d = 0; d < dn; ++d)
+            acc += (double)orc_bf16_to_f32(in[(t * H + h) * dn + d]) *
+                   (double)orc_bf16_to_f32(wd[(h * (dn + dv) + d) * R + col]);
+    } else {                    /* value side: col = d, sum over c */
+        for (int64_t c = 0; c < R; ++c)
+            acc += (double)orc_bf16_to_f32(in[(t * H + h) * R + c]) *
+                   (double)orc_bf16_to_f32(wd[(h * (dn + dv) + dn + col) * R + c]);
+    }
+    return acc;
+}
+
+static uint16_t* mla_dequant(const uint8_t* w, const float* s, int64_t H, int64_t dn, int64_t dv,
+                             int64_t R) {
+    int64_t n = H * (dn + dv);
+    uint16_t* wd = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n * R > 0 ? n * R : 1));
+    orc_weight_dequant(w, s, n, R, wd);
+    return wd;
+}
+
+/* side 0: q [T,H,dn] -> out [T,H,R]; side 1: x [T,H,R] -> out [T,H,dv]. */
+void orc_mla_absorb(int side, const uint16_t* in, const uint8_t* w, const float* s, int64_t T,
+                    int64_t H, int64_t dn, int64_t dv, int64_t R, double* out) {
+    uint16_t* wd = mla_dequant(w, s, H, dn, dv, R);
+    int64_t ncol = side == 0 ? R : dv;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t col = 0; col < ncol; ++col)
+                out[(t * H + h) * ncol + col] = mla_point(side, in, wd, H, dn, dv, R, t, h, col);
+    free(wd);
+}
+
+/* The same at (t, h, col) points. */
+void orc_mla_absorb_points(int side, const uint16_t* in, const uint8_t* w, const float* s,
+                           int64_t H, int64_t dn, int64_t dv, int64_t R, const int64_t* ts,
+                           const int64_t* hs, const int64_t* cols, int64_t npts, double* out) {
+    uint16_t* wd = mla_dequant(w, s, H, dn, dv, R);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npts; ++i)
+        out[i] = mla_point(side, in, wd, H, dn, dv, R, ts[i], hs[i], cols[i]);
+    free(wd);
+}
+
+/* ------------------------------------------------------------------------ */
 /* MoE dispatch and combine around the expert GEMMs (Admin guide 6.4 and     */
 /* 8.4: per-expert hit counts by bincount; for each expert with hits, the     */
 /* (token, slot) pairs whose routed expert it is, in token order as          */

@@ -640,3 +640,105 @@ def test_weight_quant_ue8m0_closed_forms(orc):
         for bk in range(3):
             blk = dec[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128]
             assert 224 < blk.max() <= 448
+
+
+# ------------------------------------------------------------------ MLA absorb
+
+def _torch_wkv_b(q, s, H):
+    """wkv_b dequantised by torch from the code table (float32 product, bf16
+    cast), viewed per head as the pages' absorb branch does: [H, dn+dv, R]."""
+    n, R = q.shape
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+    sf = torch.from_numpy(np.repeat(np.repeat(s, 128, 0), 128, 1)[:n, :R])
+    return (dec * sf).to(torch.bfloat16).double().view(H, n // H, R)
+
+
+@pytest.mark.parametrize("T,H,dn,dv,R", [(3, 2, 128, 128, 256), (5, 3, 128, 256, 128), (2, 2, 256, 128, 384)])
+def test_mla_absorb_matches_pages_einsums(orc, T, H, dn, dv, R):
+    """Library special case: the pages' two absorb einsums, "bshd,hdc->bshc"
+    on the key rows wkv_b[:, :dn] and "bshc,hdc->bshd" on the value rows
+    wkv_b[:, -dv:], run by torch in float64 over a torch dequantisation."""
+    rng = np.random.default_rng(T * 100 + H * 10 + dn + dv + R)
+    w = _rand_codes(rng, (H * (dn + dv), R))
+    s = (2.0 ** rng.uniform(-12, 2, (H * (dn + dv) // 128, R // 128))).astype(np.float32)
+    wkv = _torch_wkv_b(w, s, H)
+    q = inputs.bf16_bits(inputs.normal_bf16((T, H, dn), 1.0, 31))
+    x = inputs.bf16_bits(inputs.normal_bf16((T, H, R), 1.0, 32))
+    qt = torch.from_numpy(_bf16_f64(q))[:, None]                       # [b, s=1, h, d]
+    xt = torch.from_numpy(_bf16_f64(x))[:, None]
+    ref_k = torch.einsum("bshd,hdc->bshc", qt, wkv[:, :dn])[:, 0].numpy()
+    ref_v = torch.einsum("bshc,hdc->bshd", xt, wkv[:, -dv:])[:, 0].numpy()
+    bound_k = torch.einsum("bshd,hdc->bshc", qt.abs(), wkv[:, :dn].abs())[:, 0].numpy()
+    bound_v = torch.einsum("bshc,hdc->bshd", xt.abs(), wkv[:, -dv:].abs())[:, 0].numpy()
+    got_k = orc.mla_absorb(orc.MLA_KEY, q, w, s, dn, dv)
+    got_v = orc.mla_absorb(orc.MLA_VALUE, x, w, s, dn, dv)
+    assert np.all(np.abs(got_k - ref_k) <= 1e-14 * bound_k + 1e-300)
+    assert np.all(np.abs(got_v - ref_v) <= 1e-14 * bound_v + 1e-300)
+
+
+def test_mla_absorb_equals_naive(orc):
+    """The pages' statement that absorb and naive share the same math: scores
+    q_nope . k with k = W_K kv (naive: keys projected from the latent) equal
+    (absorbed q) . kv, and sum_j p_j (W_V kv_j) (naive: values, then the
+    attention average) equals W_V (sum_j p_j kv_j) (absorb).  The latent and
+    the weights p are chosen so that the averaged latent is exact in bf16."""
+    rng = np.random.default_rng(41)
+    T, H, dn, dv, R, Tk = 4, 3, 128, 128, 256, 5
+    w = _rand_codes(rng, (H * (dn + dv), R))
+    s = (2.0 ** rng.integers(-9, -2, (H * (dn + dv) // 128, R // 128))).astype(np.float32)
+    wd = _bf16_f64(orc.weight_dequant(w, s)).reshape(H, dn + dv, R)
+    q = inputs.bf16_bits(inputs.normal_bf16((T, H, dn), 1.0, 42))
+    kv = rng.integers(-8, 9, (Tk, R)).astype(np.float64)
+    # key side
+    k_naive = np.einsum("hdc,jc->jhd", wd[:, :dn], kv)
+    scores_naive = np.einsum("thd,jhd->thj", _bf16_f64(q), k_naive)
+    scores_absorb = np.einsum("thc,jc->thj", orc.mla_absorb(orc.MLA_KEY, q, w, s, dn, dv), kv)
+    mag = np.einsum("thd,jhd->thj", np.abs(_bf16_f64(q)), np.abs(np.einsum("hdc,jc->jhd", np.abs(wd[:, :dn]), np.abs(kv))))
+    assert np.all(np.abs(scores_naive - scores_absorb) <= 1e-13 * mag + 1e-300)
+    # value side: p in {0, 1/4, 1/2, 1}, so x = p . kv is a multiple of 1/4 below 2^7: exact in bf16
+    p = rng.choice([0.0, 0.25, 0.5, 1.0], (T, H, Tk))
+    x = np.einsum("thj,jc->thc", p, kv)
+    x_bits = inputs.bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+    assert np.array_equal(_bf16_f64(x_bits), x)
+    v_naive = np.einsum("hdc,jc->jhd", wd[:, dn:], kv)
+    out_naive = np.einsum("thj,jhd->thd", p, v_naive)
+    out_absorb = orc.mla_absorb(orc.MLA_VALUE, x_bits, w, s, dn, dv)
+    mag = np.einsum("thj,jhd->thd", p, np.einsum("hdc,jc->jhd", np.abs(wd[:, dn:]), np.abs(kv)))
+    assert np.all(np.abs(out_naive - out_absorb) <= 1e-13 * mag + 1e-300)
+
+
+def test_mla_absorb_one_hot(orc):
+    """A one-hot q_nope row (1.0 at d0) returns key row d0 of its head; a
+    one-hot latent row (1.0 at c0) returns column c0 of the head's value rows
+    -- exactly, and from the right head."""
+    rng = np.random.default_rng(43)
+    T, H, dn, dv, R = 2, 3, 128, 128, 384
+    w = _rand_codes(rng, (H * (dn + dv), R))
+    s = rng.uniform(0.001, 0.5, (H * (dn + dv) // 128, R // 128)).astype(np.float32)
+    wd = _bf16_f64(orc.weight_dequant(w, s))
+    q = np.zeros((T, H, dn), dtype=np.uint16)
+    x = np.zeros((T, H, R), dtype=np.uint16)
+    for t in range(T):
+        for h in range(H):
+            q[t, h, (7 * t + 3 * h) % dn] = 0x3F80
+            x[t, h, (11 * t + 5 * h + 200) % R] = 0x3F80
+    ok = orc.mla_absorb(orc.MLA_KEY, q, w, s, dn, dv)
+    ov = orc.mla_absorb(orc.MLA_VALUE, x, w, s, dn, dv)
+    for t in range(T):
+        for h in range(H):
+            assert np.array_equal(ok[t, h], wd[h * (dn + dv) + (7 * t + 3 * h) % dn])
+            c0 = (11 * t + 5 * h + 200) % R
+            assert np.array_equal(ov[t, h], wd[h * (dn + dv) + dn: (h + 1) * (dn + dv), c0])
+
+
+def test_mla_absorb_points_equal_full(orc):
+    rng = np.random.default_rng(44)
+    T, H, dn, dv, R = 6, 4, 128, 128, 256
+    w = _rand_codes(rng, (H * (dn + dv), R))
+    s = rng.uniform(0.01, 1, (H * 2, 2)).astype(np.float32)
+    q = inputs.bf16_bits(inputs.normal_bf16((T, H, dn), 1.0, 45))
+    x = inputs.bf16_bits(inputs.normal_bf16((T, H, R), 1.0, 46))
+    for side, inp, ncol in ((orc.MLA_KEY, q, R), (orc.MLA_VALUE, x, dv)):
+        full = orc.mla_absorb(side, inp, w, s, dn, dv)
+        ts, hs, cs = rng.integers(0, T, 40), rng.integers(0, H, 40), rng.integers(0, ncol, 40)
+        assert np.array_equal(orc.mla_absorb_points(side, inp, w, s, dn, dv, ts, hs, cs), full[ts, hs, cs])
