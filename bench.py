@@ -351,6 +351,42 @@ def bench_ue8m0(steps, warmup, dev, out):
         del ws, xq, xs, y
 
 
+def mla_bytes(side, T, H, dn, dv, R, out_bytes=2):
+    """Algorithmic bytes of one MLA absorb launch: the wkv_b half the side
+    reads (codes + scales), the bf16 input, the output."""
+    rows = dn if side == "key" else dv
+    w = H * rows * R + 4 * (H * rows // 128) * (R // 128)
+    width, ncol = (dn, R) if side == "key" else (R, dv)
+    return w + 2 * T * H * width + out_bytes * T * H * ncol
+
+
+def bench_mla(steps, warmup, dev, out):
+    """The MLA absorb products with an FP8 wkv_b (128 heads, dn = dv = 128,
+    kv_lora_rank 512) at a decode batch and a prefill chunk; HBM-bound."""
+    m = inputs.MLA
+    H, dn, dv, R = m["heads"], m["dn"], m["dv"], m["R"]
+    for T in (m["decode_tokens"], m["prefill_tokens"]):
+        for side in ("key", "value"):
+            nb = mla_bytes(side, T, H, dn, dv, R)
+            copies = n_copies(nb)
+            width = dn if side == "key" else R
+            sets = []
+            for c in range(copies):
+                w = inputs.normal_bf16_device((H * (dn + dv), R), 0.02,
+                                              inputs.seed_for(m["seed_id"], 1) + 100 * c, dev)
+                q, sc = fp8bs.weight_quant(w)
+                del w
+                x = inputs.normal_bf16_device((T, H, width), 1.0, inputs.seed_for(m["seed_id"], 3) + 100 * c, dev)
+                sets.append((x, q, sc))
+            y = torch.empty((T, H, R if side == "key" else dv), dtype=torch.bfloat16, device=dev)
+            fn = fp8bs.fp8bs_mla_absorb_key if side == "key" else fp8bs.fp8bs_mla_absorb_value
+            us = timed(lambda c: fn(sets[c][0], sets[c][1], sets[c][2], y, dn, dv), copies, steps, warmup)
+            flops = 2 * T * H * dn * R if side == "key" else 2 * T * H * R * dv
+            out[f"mla_absorb_{side}_T{T}_H{H}"] = row_result(
+                f"mla {side} T={T}", us, flops, nb, "hbm", {"copies": copies})
+            del sets, y
+
+
 def cpu_baseline(x_dev, w_dev, budget_s):
     """The oracle on a row sample of the prefill linear: act_quant of the
     sampled rows of x, then all N outputs of each sampled row in binary64, with
@@ -384,7 +420,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
-                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,down")
+                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,mla,down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -422,7 +458,7 @@ def main():
     rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
                                                          gemm_bytes(M, N, K), "mfma")
     sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "w8a16", "ue8m0",
-             "down"]) if args.rows == "all" else (
+             "mla", "down"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
@@ -446,6 +482,8 @@ def main():
         bench_w8a16(args.steps, args.warmup, dev, rows)
     if "ue8m0" in sel:
         bench_ue8m0(args.steps, args.warmup, dev, rows)
+    if "mla" in sel:
+        bench_mla(args.steps, args.warmup, dev, rows)
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6

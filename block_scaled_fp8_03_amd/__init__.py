@@ -30,7 +30,8 @@ __all__ = [
     "fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
     "fp8bs_moe_gemm", "fp8bs_w8a16_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter",
     "fp8bs_moe_combine", "w8a16_gemm", "fp8bs_gemm_ue8m0", "fp8bs_weight_quant_ue8m0",
-    "fp8_gemm_ue8m0", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm", "linear", "moe_route",
+    "fp8_gemm_ue8m0", "fp8bs_mla_absorb_key", "fp8bs_mla_absorb_value", "mla_absorb_key",
+    "mla_absorb_value", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "moe_gemm", "linear", "moe_route",
     "moe_quant_scatter", "moe_combine",
 ]
 
@@ -79,9 +80,12 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
     L.fp8bs_moe_quant_scatter.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     L.fp8bs_moe_combine.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
+    L.fp8bs_mla_absorb_key.argtypes = [P, I64, I64, P, P, P, I64, I64, I64, I64, I64, I, P]
+    L.fp8bs_mla_absorb_value.argtypes = [P, I64, I64, P, P, P, I64, I64, I64, I64, I64, I, P]
     for fn in ("fp8bs_act_quant", "fp8bs_weight_quant", "fp8bs_weight_dequant", "fp8bs_gemm",
                "fp8bs_moe_gemm", "fp8bs_w8a16_gemm", "fp8bs_moe_route", "fp8bs_moe_quant_scatter",
-               "fp8bs_moe_combine", "fp8bs_gemm_ue8m0", "fp8bs_weight_quant_ue8m0"):
+               "fp8bs_moe_combine", "fp8bs_gemm_ue8m0", "fp8bs_weight_quant_ue8m0",
+               "fp8bs_mla_absorb_key", "fp8bs_mla_absorb_value"):
         getattr(L, fn).restype = I
     _lib = L
     return L
@@ -340,6 +344,52 @@ def moe_combine(out: torch.Tensor, w: torch.Tensor, row_of: torch.Tensor,
     y = torch.empty((w.shape[0], out.shape[1]), dtype=out_dtype, device=out.device)
     fp8bs_moe_combine(out, w, row_of, y)
     return y
+
+
+def _fp8bs_mla(fn: str, inp: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, out: torch.Tensor,
+               dn: int, dv: int, value_side: bool) -> None:
+    if inp.dim() != 3 or w.dim() != 2:
+        raise ValueError("input must be [T, H, width] and wkv_b [H*(dn+dv), R]")
+    T, H, width = inp.shape
+    R = w.shape[1]
+    if w.shape[0] != H * (dn + dv) or width != (R if value_side else dn):
+        raise ValueError("wkv_b must be [H*(dn+dv), R]; q [T, H, dn] or x [T, H, R]")
+    if tuple(w_s.shape) != (-(-w.shape[0] // BLOCK), -(-R // BLOCK)):
+        raise ValueError("wkv_b_s must be [H*(dn+dv)/128, R/128]")
+    if tuple(out.shape) != (T, H, dv if value_side else R):
+        raise ValueError("out shape mismatch")
+    if inp.dtype != torch.bfloat16 or not inp.is_cuda or (width > 1 and inp.stride(2) != 1):
+        raise ValueError("input must be a bf16 device tensor with a contiguous last dimension")
+    _call(fn, inp.data_ptr(), inp.stride(0), inp.stride(1), _need(w, _F8, "wkv_b"),
+          _need(w_s, (torch.float32,), "wkv_b_s"), _need(out, (torch.bfloat16, torch.float32), "out"),
+          T, H, dn, dv, R, _out_code(out), _stream(inp))
+
+
+def fp8bs_mla_absorb_key(q: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, out: torch.Tensor,
+                         dn: int, dv: int) -> None:
+    """q bf16 [T, H, dn] (strided token/head dims allowed, e.g. the q_nope
+    slice of q) -> out [T, H, R] = q_nope absorbed through the key rows of
+    the FP8 wkv_b [H*(dn+dv), R]."""
+    _fp8bs_mla("fp8bs_mla_absorb_key", q, w, w_s, out, dn, dv, False)
+
+
+def fp8bs_mla_absorb_value(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, out: torch.Tensor,
+                           dn: int, dv: int) -> None:
+    """x bf16 [T, H, R] (the attention-weighted latent) -> out [T, H, dv]
+    through the value rows of the FP8 wkv_b [H*(dn+dv), R]."""
+    _fp8bs_mla("fp8bs_mla_absorb_value", x, w, w_s, out, dn, dv, True)
+
+
+def mla_absorb_key(q, w, w_s, dn: int, dv: int, out_dtype=torch.bfloat16) -> torch.Tensor:
+    out = torch.empty((q.shape[0], q.shape[1], w.shape[1]), dtype=out_dtype, device=q.device)
+    fp8bs_mla_absorb_key(q, w, w_s, out, dn, dv)
+    return out
+
+
+def mla_absorb_value(x, w, w_s, dn: int, dv: int, out_dtype=torch.bfloat16) -> torch.Tensor:
+    out = torch.empty((x.shape[0], x.shape[1], dv), dtype=out_dtype, device=x.device)
+    fp8bs_mla_absorb_value(x, w, w_s, out, dn, dv)
+    return out
 
 
 def w8a16_gemm(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, out_dtype=torch.bfloat16) -> torch.Tensor:

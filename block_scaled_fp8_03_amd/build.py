@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8bs.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "gemm.hip", "moe_dispatch.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "moe_dispatch.hip", "mla.hip", "abi.cpp"]
 
 COMMON_FLAGS = [
     "-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -191,6 +191,53 @@ int fp8bs_w8a16_gemm(const void* x_bf16, const void* w_e4m3, const float* w_s, v
                                             out_dtype == FP8BS_OUT_F32, (hipStream_t)stream));
 }
 
+static int mla_entry(bool value_side, const void* in, int64_t ld_t, int64_t ld_h, const void* w,
+                     const float* w_s, void* out, int64_t T, int64_t H, int64_t dn, int64_t dv,
+                     int64_t R, int out_dtype, void* stream) {
+  if (T < 0 || H < 0 || ld_t < 0 || ld_h < 0 || dn <= 0 || dv <= 0 || R <= 0 || dn % 128 != 0 ||
+      dv % 128 != 0 || R % 128 != 0)
+    return FP8BS_ERR_SHAPE;
+  if (value_side ? R > 512 : (dn != 128 && dn != 256)) return FP8BS_ERR_SHAPE;
+  if (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_F32) return FP8BS_ERR_ENUM;
+  if (ld_t % 8 != 0 || ld_h % 8 != 0) return FP8BS_ERR_ALIGN;
+  const int64_t width = value_side ? R : dn, ncol = value_side ? dv : R;
+  const int64_t nrows = mul(H, dn + dv), nw = mul(nrows, R), nout = mul(mul(T, H), ncol);
+  // every element offset the kernels form fits an int
+  if (nrows < 0 || nw < 0 || nout < 0 || nw > kLimitInt || nout > kLimitInt || ld_t > kLimitInt ||
+      ld_h > kLimitInt || dn + dv > kLimitInt)
+    return FP8BS_ERR_SHAPE;
+  if (nout == 0) return FP8BS_OK;
+  const int64_t nin = mul(T - 1, ld_t) + mul(H - 1, ld_h) + width;   // input extent (elements)
+  if (nin > kLimitInt || mul(H, cdiv(T, 256)) > kLimitInt) return FP8BS_ERR_SHAPE;
+  if (!in || !w || !w_s || !out) return FP8BS_ERR_NULL;
+  if (!aligned(in, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(w_s, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t ob = nout * (out_dtype == FP8BS_OUT_F32 ? 4 : 2);
+  const int64_t nws = (nrows / 128) * (R / 128) * 4;
+  if (overlap(out, ob, in, 2 * nin) || overlap(out, ob, w, nw) || overlap(out, ob, w_s, nws))
+    return FP8BS_ERR_ALIAS;
+  const bool f32 = out_dtype == FP8BS_OUT_F32;
+  return status_of(value_side
+                       ? fp8bs::launch_mla_absorb_value(in, ld_t, ld_h, w, w_s, out, T, H, dn, dv,
+                                                        R, f32, (hipStream_t)stream)
+                       : fp8bs::launch_mla_absorb_key(in, ld_t, ld_h, w, w_s, out, T, H, dn, dv, R,
+                                                      f32, (hipStream_t)stream));
+}
+
+int fp8bs_mla_absorb_key(const void* q_bf16, int64_t ld_t, int64_t ld_h, const void* wkv_b,
+                         const float* wkv_b_s, void* out, int64_t T, int64_t H, int64_t dn,
+                         int64_t dv, int64_t R, int out_dtype, void* stream) {
+  return mla_entry(false, q_bf16, ld_t, ld_h, wkv_b, wkv_b_s, out, T, H, dn, dv, R, out_dtype,
+                   stream);
+}
+
+int fp8bs_mla_absorb_value(const void* x_bf16, int64_t ld_t, int64_t ld_h, const void* wkv_b,
+                           const float* wkv_b_s, void* out, int64_t T, int64_t H, int64_t dn,
+                           int64_t dv, int64_t R, int out_dtype, void* stream) {
+  return mla_entry(true, x_bf16, ld_t, ld_h, wkv_b, wkv_b_s, out, T, H, dn, dv, R, out_dtype,
+                   stream);
+}
+
 int64_t fp8bs_moe_route_workspace_size(int64_t T, int64_t topk, int64_t E) {
   if (T < 0 || topk < 1 || E < 1 || E > kLimitInt) return -1;
   const int64_t P = mul(T, topk);

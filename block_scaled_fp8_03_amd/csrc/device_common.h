@@ -91,4 +91,23 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// 8 e4m3 codes (two dwords, byte order = element order) times a block scale
+// -> 8 bf16, with weight_dequant's rounding: the float32 product (exact
+// decode, one RN32 multiply) then bf16 round-to-nearest-even.
+__device__ __forceinline__ v8bf dequant8_bf16(uint32_t w0, uint32_t w1, float sc) {
+  const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const v2f d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+  const v4u_t u = {pack2_bf16(__fmul_rn(a.x, sc), __fmul_rn(a.y, sc)),
+                   pack2_bf16(__fmul_rn(b.x, sc), __fmul_rn(b.y, sc)),
+                   pack2_bf16(__fmul_rn(c.x, sc), __fmul_rn(c.y, sc)),
+                   pack2_bf16(__fmul_rn(d.x, sc), __fmul_rn(d.y, sc))};
+  return __builtin_bit_cast(v8bf, u);
+}
+
 }  // namespace fp8bs

@@ -415,8 +415,6 @@ gemm_tile_kernel(GemmParams p) {
 // partial is then scaled and added in fp32 as in the tile kernel.  K mapping:
 // instruction i, lane group g takes the bytes [32g + 8i, 32g + 8i + 8) of the
 // block for both operands.
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Eight e4m3 bytes (two dwords, byte order = element order) -> eight bf16.
 __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -630,19 +628,6 @@ gemm_decode_kernel(GemmParams p, int rows) {
 // fragment reads conflict-free under the same bank rule.
 __device__ __forceinline__ int swz64(int r) { return (r >> 1) & 2; }
 
-// 8 e4m3 codes (byte order = element order) times s -> 8 bf16 (two roundings)
-__device__ __forceinline__ v8bf dequant8_bf16(uint32_t w0, uint32_t w1, float sc) {
-  const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-  const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-  const v2f d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-  typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
-  const v4u_t u = {pack2_bf16(__fmul_rn(a.x, sc), __fmul_rn(a.y, sc)),
-                   pack2_bf16(__fmul_rn(b.x, sc), __fmul_rn(b.y, sc)),
-                   pack2_bf16(__fmul_rn(c.x, sc), __fmul_rn(c.y, sc)),
-                   pack2_bf16(__fmul_rn(d.x, sc), __fmul_rn(d.y, sc))};
-  return __builtin_bit_cast(v8bf, u);
-}
 
 template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC, bool OUT_F32>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))

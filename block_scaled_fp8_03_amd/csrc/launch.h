@@ -35,5 +35,11 @@ hipError_t launch_moe_route(const int32_t* indices, int64_t T, int64_t topk, int
 hipError_t launch_moe_combine(const void* out, const float* w, const int32_t* row_of, void* y,
                               int64_t T, int64_t topk, int64_t R, int64_t N, bool out_f32,
                               hipStream_t stream);
+hipError_t launch_mla_absorb_key(const void* q, int64_t ld_t, int64_t ld_h, const void* w,
+                                 const float* ws, void* out, int64_t T, int64_t H, int64_t dn,
+                                 int64_t dv, int64_t R, bool out_f32, hipStream_t stream);
+hipError_t launch_mla_absorb_value(const void* x, int64_t ld_t, int64_t ld_h, const void* w,
+                                   const float* ws, void* out, int64_t T, int64_t H, int64_t dn,
+                                   int64_t dv, int64_t R, bool out_f32, hipStream_t stream);
 
 }  // namespace fp8bs

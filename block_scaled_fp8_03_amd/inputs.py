@@ -114,3 +114,11 @@ CONFIGS = {
             dequant=dict(N=18432, K=7168), gemms=[dict(N=1536, K=7168), dict(N=16384, K=512)],
             x_std=1.0, w_std=0.02, fmt="ue8m0"),
 }
+
+# The MLA absorb products (workload id 6 in the seed recipe): the attention
+# shape the pages' configurations share (qk_nope_head_dim 128, v_head_dim 128,
+# kv_lora_rank 512) with the 671B model's 128 heads, wkv_b drawn like the other
+# weights (std 0.02) and N(0, 1) activations, at a decode batch of 32 tokens and
+# a 4096-token prefill.
+MLA = dict(name="MLA absorb with an FP8 wkv_b", heads=128, dn=128, dv=128, R=512,
+           decode_tokens=32, prefill_tokens=4096, x_std=1.0, w_std=0.02, seed_id=6)

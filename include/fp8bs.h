@@ -266,6 +266,43 @@ int fp8bs_moe_quant_scatter(const void* x_bf16, const int32_t* row_of, void* q_e
 int fp8bs_moe_combine(const void* out_bf16, const float* w, const int32_t* row_of, void* y,
                       int64_t T, int64_t topk, int64_t R, int64_t N, int out_dtype, void* stream);
 
+/*
+ * MLA absorb with an FP8 wkv_b -- the two products of the absorb attention
+ * (Admin guide 8.3, steps 5 and 7) that use the up-projection wkv_b
+ * [H*(dn+dv), R] viewed per head as [H, dn+dv, R].  With an FP8 wkv_b the
+ * pages dequantise the whole weight (weight_dequant, 8.5.2) on every forward
+ * step and then run the einsums; here the kernels dequantise in registers
+ * with the same rounding (bf16(RN32(decode(q) * s))) and multiply with bf16
+ * MFMA, accumulating in float32; the bf16 weight is never stored.
+ *
+ * mla_absorb_key -- q_nope carried into the latent space by the key rows:
+ *   out[t, h, c] = sum_{d < dn} q[t, h, d] * Wd[h*(dn+dv) + d, c]
+ * mla_absorb_value -- the attention-weighted latent turned into values by
+ * the value rows:
+ *   out[t, h, d] = sum_{c < R} x[t, h, c] * Wd[h*(dn+dv) + dn + d, c]
+ *
+ *   q_bf16 / x_bf16  in   bf16, element (t, h, i) at [t*ld_t + h*ld_h + i]
+ *                         for i < dn (key) or i < R (value); ld_t, ld_h >= 0
+ *                         and multiples of 8 (so the q_nope slice of a
+ *                         [T, H, dn + rope] q can be passed in place)
+ *   wkv_b            in   e4m3 [H*(dn+dv), R]
+ *   wkv_b_s          in   float32 [H*(dn+dv)/128, R/128]
+ *   out              out  contiguous [T, H, R] (key) or [T, H, dv] (value),
+ *                         bf16 or float32 (out_dtype)
+ *   dn, dv, R positive multiples of 128 (the pages' configurations all use
+ *   128, 128, 512); key side: dn is 128 or 256; value side: R <= 512.
+ *   T, H >= 0 (either 0 = no-op); the weight, the output and the input's
+ *   extent below 2^31 elements.
+ * Input, wkv_b and out 16-byte aligned, wkv_b_s 4-byte aligned; out must not
+ * overlap an input (FP8BS_ERR_ALIAS).
+ */
+int fp8bs_mla_absorb_key(const void* q_bf16, int64_t ld_t, int64_t ld_h, const void* wkv_b,
+                         const float* wkv_b_s, void* out, int64_t T, int64_t H, int64_t dn,
+                         int64_t dv, int64_t R, int out_dtype, void* stream);
+int fp8bs_mla_absorb_value(const void* x_bf16, int64_t ld_t, int64_t ld_h, const void* wkv_b,
+                           const float* wkv_b_s, void* out, int64_t T, int64_t H, int64_t dn,
+                           int64_t dv, int64_t R, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,3 +165,39 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         fp8bs.act_quant(x)
+
+
+@pytest.mark.parametrize("name", ["fp8bs_mla_absorb_key", "fp8bs_mla_absorb_value"])
+def test_mla_absorb_validation(L, name):
+    f = getattr(L, name)
+    H, dn, dv, R = 4, 128, 128, 512
+    ld_t, ld_h = H * (R if name.endswith("value") else dn), (R if name.endswith("value") else dn)
+    ok = (P0, ld_t, ld_h, P1, P2, P3, 8, H, dn, dv, R, 0, None)
+
+    def call(**kw):
+        names = ("inp", "ld_t", "ld_h", "w", "ws", "out", "T", "H", "dn", "dv", "R", "dt", "st")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    assert call(T=-1) == SHAPE
+    assert call(dn=100) == SHAPE
+    assert call(dv=0) == SHAPE
+    assert call(R=0) == SHAPE
+    assert call(ld_h=-8) == SHAPE
+    if name.endswith("value"):
+        assert call(R=640) == SHAPE                     # value side: R <= 512
+    else:
+        assert call(dn=384) == SHAPE                    # key side: dn is 128 or 256
+    assert call(dt=2) == ENUM
+    assert call(ld_t=ld_t + 4) == ALIGN
+    assert call(ld_h=12) == ALIGN
+    assert call(inp=P0 + 2) == ALIGN
+    assert call(ws=P2 + 2) == ALIGN
+    assert call(out=P3 + 8) == ALIGN
+    assert call(w=None) == NULL
+    assert call(out=P0) == ALIAS                        # out over the input
+    assert call(out=P1 + 64) == ALIAS                   # out inside wkv_b
+    assert call(inp=None, w=None, ws=None, out=None, T=0) == OK
+    assert call(inp=None, w=None, ws=None, out=None, H=0) == OK
+    assert call(H=1 << 20, T=1 << 12) == SHAPE          # output beyond 2^31 elements
