@@ -68,14 +68,22 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 // lds + size * i.  Written as inline assembly so the compiler does not treat
 // every later LDS read as dependent on every load in flight; completion is
 // tracked explicitly with wait_vmcnt() before the barrier that publishes a
-// stage.
+// stage.  The LDS address is wave-uniform (it goes to M0); readfirstlane
+// keeps it in an SGPR whatever register the compiler chose for it.
 __device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+// The same with the non-temporal hint, for data read exactly once (the
+// weight stream of the decode kernel): measured 27.4 vs 29.4 us on the
+// decode-shaped GEMM.
+__device__ __forceinline__ void dma_b128_nt(v4i rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 __device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -608,6 +616,213 @@ gemm_decode_kernel(GemmParams p, int rows) {
 }
 
 // ----------------------------------------------------------------------------
+// Decode kernel, eight-wave form (M <= 32).
+// ----------------------------------------------------------------------------
+// Workgroup g owns `rows` (<= 72, a multiple of 8) consecutive weight rows and
+// all M activation rows, one workgroup per CU.  A stage holds KPS = 4
+// consecutive K blocks: the weight rows ([4][72 rows][128 B], non-temporal
+// DMA), the activations ([4][16 MT rows][128 B]), their scales ([4][64]) and
+// the (at most two) weight block scales the rows touch -- 54.5 KB for
+// M <= 32, three stages (two in flight, ~107 KB per CU).  Every wave issues
+// exactly LPS = 8 DMA instructions per stage (57 real ones, padded with
+// zero-filling out-of-range loads into a 256-byte dummy area), so one vmcnt
+// bound fits all waves.
+// Wave w computes K block w % 4 of each stage for the 16-row weight tiles
+// 0..2 (w < 4) or 3..4 (w >= 4): the two waves that share a SIMD cover all
+// five tiles of one K block (72 rows; rows 72..79 of tile 4 read other LDS
+// data and are never stored).  The four waves of a tile set are summed
+// through LDS at the end.  Arithmetic as in the four-wave kernel: e4m3 to
+// bf16 (exact), bf16 MFMA, one scale fold per K block.
+constexpr int kDecode8Rows = 72;
+
+template <int MT, bool OUT_F32>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_decode8_kernel(GemmParams p, int rows) {
+  constexpr int NW = 8, KPS = 4, ST = 3, MR = 16 * MT, LPS = 8;
+  constexpr int GRP = kDecode8Rows / 8;                           // weight row groups per K block
+  constexpr int AGRP = MR / 8;                                    // activation row groups
+  constexpr int B_TILE = kDecode8Rows * 128, A_TILE = MR * 128;   // one K block
+  constexpr int B_BYTES = KPS * B_TILE, A_BYTES = KPS * A_TILE;
+  constexpr int AS_BYTES = KPS * 256, BS_BYTES = 256;
+  constexpr int STAGE = B_BYTES + A_BYTES + AS_BYTES + BS_BYTES;
+  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP, N_REAL = N_B + N_A + KPS + 1;
+  constexpr int NTW = 3;                                          // tiles per wave (set 1: 2)
+  static_assert(N_REAL <= NW * LPS && MR <= 32, "shape");
+  static_assert(ST * STAGE + 256 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 256];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int M = p.rows, N = p.N, K = p.K;
+  const int nkb = K / 128, nkc = (nkb + KPS - 1) / KPS;
+  const int n_base = blockIdx.x * rows;
+  const int n_end = min(n_base + rows, N);
+  const int q = wave & 3;                                 // this wave's K block in a stage
+  const int jt0 = 3 * (wave >> 2);                        // this wave's first tile
+  const int ntw = wave < 4 ? 3 : 2;
+
+  const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)M * K));
+  const v4i b_rsrc = make_rsrc(p.b, (uint32_t)((int64_t)N * K));
+  const v4i as_rsrc = make_rsrc(p.a_s, (uint32_t)((int64_t)M * nkb * 4));
+  const int nbn = (N + 127) / 128;
+  const v4i bs_rsrc = make_rsrc(p.b_s, (uint32_t)((int64_t)nbn * nkb * 4));
+  const uint32_t smem_lds = lds_addr(smem);
+  const uint32_t dummy_lds = smem_lds + ST * STAGE;
+
+  // DMA instruction u = wave + NW i of a stage (wave-uniform type):
+  //   u < N_B                weight rows: K block u / GRP, row group u % GRP
+  //   u < N_B + N_A          activations: K block v / AGRP, row group v % AGRP
+  //   u < N_B + N_A + KPS    a_s of K block u - N_B - N_A, lane = activation row
+  //   u == N_B + N_A + KPS   b_s: lane l < 8 -> K block (l >> 1) & 3, block l & 1
+  //   otherwise              padding (out of range -> zeros into the dummy area)
+  // 16-byte loads: lane l takes row l / 8 of its group and logical chunk
+  // (l % 8) ^ (l / 8), the row's swizzle (row % 8 = l / 8).
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  uint32_t voff[LPS], lds_off[LPS], kstep[LPS];
+#pragma unroll
+  for (int i = 0; i < LPS; ++i) {
+    const int u = wave + NW * i;
+    if (u < N_B) {
+      const int kq = u / GRP, grp = u % GRP;
+      voff[i] = 8 * grp < rows ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq
+                               : 0xF0000000u;
+      lds_off[i] = kq * B_TILE + grp * 1024;
+      kstep[i] = KPS * 128;
+    } else if (u < N_B + N_A) {
+      const int v = u - N_B, kq = v / AGRP, grp = v % AGRP;
+      voff[i] = (uint32_t)(8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq;
+      lds_off[i] = B_BYTES + kq * A_TILE + grp * 1024;
+      kstep[i] = KPS * 128;
+    } else if (u < N_B + N_A + KPS) {
+      const int kq = u - N_B - N_A;
+      voff[i] = (uint32_t)lane * nkb * 4 + 4 * kq;
+      lds_off[i] = B_BYTES + A_BYTES + kq * 256;
+      kstep[i] = KPS * 4;
+    } else if (u == N_B + N_A + KPS) {
+      const int blk = n_base / 128 + (lane & 1);
+      voff[i] = lane < 8 && blk < nbn ? (uint32_t)blk * nkb * 4 + 4 * ((lane >> 1) & 3) : 0xF0000000u;
+      lds_off[i] = B_BYTES + A_BYTES + AS_BYTES;
+      kstep[i] = KPS * 4;
+    } else {
+      voff[i] = 0xF0000000u;
+      lds_off[i] = 0;
+      kstep[i] = 0;
+    }
+  }
+
+  auto issue = [&](int kc, int st) {
+    const uint32_t base = smem_lds + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int u = wave + NW * i;                        // wave-uniform: scalar branches
+      const uint32_t off = voff[i] + (uint32_t)kc * kstep[i];
+      if (u < N_B) dma_b128_nt(b_rsrc, base + lds_off[i], off);
+      else if (u < N_B + N_A) dma_b128(a_rsrc, base + lds_off[i], off);
+      else if (u < N_B + N_A + KPS) dma_b32(as_rsrc, base + lds_off[i], off);
+      else if (u == N_B + N_A + KPS) dma_b32(bs_rsrc, base + lds_off[i], off);
+      else dma_b32(as_rsrc, dummy_lds, 0xF0000000u);
+    }
+  };
+
+  v4f acc[NTW][MT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nkc) issue(s, s);
+
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int st = kc % ST;
+    if (kc + ST - 2 < nkc) wait_vmcnt<(ST - 2) * LPS>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (kc + ST - 1 < nkc) issue(kc + ST - 1, (kc + ST - 1) % ST);
+    if (kc * KPS + q >= nkb) continue;                   // tail stage: K block past the end
+    const uint8_t* base = smem + st * STAGE;
+    const uint8_t* bt = base + q * B_TILE;
+    const uint8_t* at = base + B_BYTES + q * A_TILE;
+    const float* ast = (const float*)(base + B_BYTES + A_BYTES + q * 256);
+    const float* bst = (const float*)(base + B_BYTES + A_BYTES + AS_BYTES);
+    v8bf af[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const v8i f = lds_frag<0>(at, 16 * t + r16, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[t][i] = e4m3x8_to_bf16(f[2 * i], f[2 * i + 1]);
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      if (j >= ntw) break;                                 // wave-uniform
+      const v8i f = lds_frag<0>(bt, 16 * (jt0 + j) + r16, g);
+      const int nl = n_base + 16 * (jt0 + j) + 4 * g;      // this lane's four rows share a block
+      const float bsv = bst[2 * q + ((nl / 128 - n_base / 128) & 1)];
+      v8bf bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bf[i] = e4m3x8_to_bf16(f[2 * i], f[2 * i + 1]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        v4f pr = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], af[t][i], pr, 0, 0, 0);
+        const float sc = ast[16 * t + r16] * bsv;
+        acc[j][t][0] = __builtin_fmaf(pr[0], sc, acc[j][t][0]);
+        acc[j][t][1] = __builtin_fmaf(pr[1], sc, acc[j][t][1]);
+        acc[j][t][2] = __builtin_fmaf(pr[2], sc, acc[j][t][2]);
+        acc[j][t][3] = __builtin_fmaf(pr[3], sc, acc[j][t][3]);
+      }
+    }
+  }
+
+  // ---- reduction over the four K-block waves of each tile set, then store
+  constexpr int NV = NTW * MT * 4;
+  float* red = (float*)smem;                             // [NW][NV][64], reused
+  static_assert(NW * NV * 64 * 4 <= ST * STAGE, "reduction area");
+  barrier_lds();
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * NV + (j * MT + t) * 4 + r) * 64 + lane] = acc[j][t][r];
+  barrier_lds();
+  if (q != 0) return;
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    if (j >= ntw) break;
+    const int n = n_base + 16 * (jt0 + j) + 4 * g;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = 16 * t + r16;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[j][t][r];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) v[r] += red[((wave + w) * NV + (j * MT + t) * 4 + r) * 64 + lane];
+      }
+      if (m >= M || n >= n_end) continue;
+      if (OUT_F32) {
+        float* cp = (float*)p.c + (int64_t)m * N + n;
+        if ((N % 4) == 0 && n + 3 < n_end) *(float4*)cp = make_float4(v[0], v[1], v[2], v[3]);
+        else for (int r = 0; r < 4; ++r) if (n + r < n_end) cp[r] = v[r];
+      } else {
+        uint16_t* cp = (uint16_t*)p.c + (int64_t)m * N + n;
+        const uint32_t lo = pack2_bf16(v[0], v[1]), hi = pack2_bf16(v[2], v[3]);
+        if ((N % 4) == 0 && n + 3 < n_end) *(uint2*)cp = make_uint2(lo, hi);
+        else {
+          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+          for (int r = 0; r < 4; ++r) if (n + r < n_end) cp[r] = h[r];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // BF16 path (W8A16): C = x . weight_dequant(W)^T with x bf16, W e4m3 + 128x128
 // block scales ("DeepSeek-V3 Administrator & Developer Guide" 6.3: with
 // gemm_impl "bf16" the FP8 weight is dequantised (8.5.2) and the linear runs
@@ -807,9 +1022,19 @@ int device_cus() {
 
 template <int MT>
 hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
-  // rows per workgroup: a multiple of 8 that spreads N over the CUs, at most 80
   const int cus = device_cus();
   const int groups = (p.N + 7) / 8;
+  if constexpr (MT <= 2) {
+    // eight-wave kernel: rows per workgroup a multiple of 8, at most 72
+    const int rows = 8 * std::min(kDecode8Rows / 8, (groups + cus - 1) / cus);
+    const int grid = (p.N + rows - 1) / rows;
+    if (out_f32)
+      gemm_decode8_kernel<MT, true><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    else
+      gemm_decode8_kernel<MT, false><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    return hipGetLastError();
+  }
+  // rows per workgroup: a multiple of 8 that spreads N over the CUs, at most 80
   const int rows = 8 * std::min(kDecodeMaxRows / 8, (groups + cus - 1) / cus);
   const int grid = (p.N + rows - 1) / rows;
   if (out_f32)
