@@ -623,10 +623,13 @@ gemm_decode_kernel(GemmParams p, int rows) {
 // consecutive K blocks: the weight rows ([4][72 rows][128 B], non-temporal
 // DMA), the activations ([4][16 MT rows][128 B]), their scales ([4][64]) and
 // the (at most two) weight block scales the rows touch -- 54.5 KB for
-// M <= 32, three stages (two in flight, ~107 KB per CU).  Every wave issues
-// exactly LPS = 8 DMA instructions per stage (57 real ones, padded with
-// zero-filling out-of-range loads into a 256-byte dummy area), so one vmcnt
-// bound fits all waves.
+// M <= 32, three stages (two in flight, ~107 KB per CU).  The activation
+// scales of a stage come as 16 bytes per row (one load; CH = true, needs K/128
+// a multiple of 4 and a 16-byte aligned a_s) or as four column loads; the two
+// weight block scales are read with scalar loads.  Every wave issues exactly
+// LPS DMA instructions per stage (the real ones padded with zero-filling
+// out-of-range loads into a 256-byte dummy area), so one vmcnt bound fits all
+// waves.
 // Wave w computes K block w % 4 of each stage for the 16-row weight tiles
 // 0..2 (w < 4) or 3..4 (w >= 4): the two waves that share a SIMD cover all
 // five tiles of one K block (72 rows; rows 72..79 of tile 4 read other LDS
@@ -635,17 +638,19 @@ gemm_decode_kernel(GemmParams p, int rows) {
 // bf16 (exact), bf16 MFMA, one scale fold per K block.
 constexpr int kDecode8Rows = 72;
 
-template <int MT, bool OUT_F32>
+template <int MT, bool OUT_F32, bool CH>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_decode8_kernel(GemmParams p, int rows) {
-  constexpr int NW = 8, KPS = 4, ST = 3, MR = 16 * MT, LPS = 8;
+  constexpr int NW = 8, KPS = 4, ST = 3, MR = 16 * MT;
   constexpr int GRP = kDecode8Rows / 8;                           // weight row groups per K block
   constexpr int AGRP = MR / 8;                                    // activation row groups
   constexpr int B_TILE = kDecode8Rows * 128, A_TILE = MR * 128;   // one K block
   constexpr int B_BYTES = KPS * B_TILE, A_BYTES = KPS * A_TILE;
-  constexpr int AS_BYTES = KPS * 256, BS_BYTES = 256;
-  constexpr int STAGE = B_BYTES + A_BYTES + AS_BYTES + BS_BYTES;
-  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP, N_REAL = N_B + N_A + KPS + 1;
+  constexpr int AS_BYTES = KPS * 256;                             // [row][4] or [4][row]
+  constexpr int STAGE = B_BYTES + A_BYTES + AS_BYTES;
+  constexpr int N_AS = CH ? 1 : KPS;
+  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP, N_REAL = N_B + N_A + N_AS;
+  constexpr int LPS = (N_REAL + NW - 1) / NW;
   constexpr int NTW = 3;                                          // tiles per wave (set 1: 2)
   static_assert(N_REAL <= NW * LPS && MR <= 32, "shape");
   static_assert(ST * STAGE + 256 <= 160 * 1024, "LDS");
@@ -666,15 +671,16 @@ gemm_decode8_kernel(GemmParams p, int rows) {
   const v4i b_rsrc = make_rsrc(p.b, (uint32_t)((int64_t)N * K));
   const v4i as_rsrc = make_rsrc(p.a_s, (uint32_t)((int64_t)M * nkb * 4));
   const int nbn = (N + 127) / 128;
-  const v4i bs_rsrc = make_rsrc(p.b_s, (uint32_t)((int64_t)nbn * nkb * 4));
+  typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+  const const_f32_ptr bs_const = (const_f32_ptr)(uintptr_t)p.b_s;
   const uint32_t smem_lds = lds_addr(smem);
   const uint32_t dummy_lds = smem_lds + ST * STAGE;
 
   // DMA instruction u = wave + NW i of a stage (wave-uniform type):
   //   u < N_B                weight rows: K block u / GRP, row group u % GRP
   //   u < N_B + N_A          activations: K block v / AGRP, row group v % AGRP
-  //   u < N_B + N_A + KPS    a_s of K block u - N_B - N_A, lane = activation row
-  //   u == N_B + N_A + KPS   b_s: lane l < 8 -> K block (l >> 1) & 3, block l & 1
+  //   u < N_B + N_A + N_AS   a_s: CH: lane = row, its 4 K blocks (16 bytes);
+  //                          else K block u - N_B - N_A, lane = activation row
   //   otherwise              padding (out of range -> zeros into the dummy area)
   // 16-byte loads: lane l takes row l / 8 of its group and logical chunk
   // (l % 8) ^ (l / 8), the row's swizzle (row % 8 = l / 8).
@@ -694,15 +700,10 @@ gemm_decode8_kernel(GemmParams p, int rows) {
       voff[i] = (uint32_t)(8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq;
       lds_off[i] = B_BYTES + kq * A_TILE + grp * 1024;
       kstep[i] = KPS * 128;
-    } else if (u < N_B + N_A + KPS) {
-      const int kq = u - N_B - N_A;
+    } else if (u < N_B + N_A + N_AS) {
+      const int kq = CH ? 0 : u - N_B - N_A;
       voff[i] = (uint32_t)lane * nkb * 4 + 4 * kq;
       lds_off[i] = B_BYTES + A_BYTES + kq * 256;
-      kstep[i] = KPS * 4;
-    } else if (u == N_B + N_A + KPS) {
-      const int blk = n_base / 128 + (lane & 1);
-      voff[i] = lane < 8 && blk < nbn ? (uint32_t)blk * nkb * 4 + 4 * ((lane >> 1) & 3) : 0xF0000000u;
-      lds_off[i] = B_BYTES + A_BYTES + AS_BYTES;
       kstep[i] = KPS * 4;
     } else {
       voff[i] = 0xF0000000u;
@@ -719,9 +720,10 @@ gemm_decode8_kernel(GemmParams p, int rows) {
       const uint32_t off = voff[i] + (uint32_t)kc * kstep[i];
       if (u < N_B) dma_b128_nt(b_rsrc, base + lds_off[i], off);
       else if (u < N_B + N_A) dma_b128(a_rsrc, base + lds_off[i], off);
-      else if (u < N_B + N_A + KPS) dma_b32(as_rsrc, base + lds_off[i], off);
-      else if (u == N_B + N_A + KPS) dma_b32(bs_rsrc, base + lds_off[i], off);
-      else dma_b32(as_rsrc, dummy_lds, 0xF0000000u);
+      else if (u < N_B + N_A + N_AS) {
+        if (CH) dma_b128(as_rsrc, base + lds_off[i], off);
+        else dma_b32(as_rsrc, base + lds_off[i], off);
+      } else dma_b32(as_rsrc, dummy_lds, 0xF0000000u);
     }
   };
 
@@ -745,8 +747,16 @@ gemm_decode8_kernel(GemmParams p, int rows) {
     const uint8_t* base = smem + st * STAGE;
     const uint8_t* bt = base + q * B_TILE;
     const uint8_t* at = base + B_BYTES + q * A_TILE;
-    const float* ast = (const float*)(base + B_BYTES + A_BYTES + q * 256);
-    const float* bst = (const float*)(base + B_BYTES + A_BYTES + AS_BYTES);
+    const float* ast = (const float*)(base + B_BYTES + A_BYTES);
+    // the (at most two) weight block scales of this K block, read with scalar
+    // loads (constant address space, wave-uniform index) so that no vector
+    // load -- and no compiler-inserted vmcnt wait -- enters the K loop; the
+    // second index is clamped (when the rows do not reach a second block no
+    // lane uses it)
+    const int kbq = kc * KPS + q;
+    const int blk0 = n_base / 128, blk1 = min(blk0 + 1, nbn - 1);
+    const float bs0 = bs_const[__builtin_amdgcn_readfirstlane(blk0 * nkb + kbq)];
+    const float bs1 = bs_const[__builtin_amdgcn_readfirstlane(blk1 * nkb + kbq)];
     v8bf af[MT][4];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -759,7 +769,7 @@ gemm_decode8_kernel(GemmParams p, int rows) {
       if (j >= ntw) break;                                 // wave-uniform
       const v8i f = lds_frag<0>(bt, 16 * (jt0 + j) + r16, g);
       const int nl = n_base + 16 * (jt0 + j) + 4 * g;      // this lane's four rows share a block
-      const float bsv = bst[2 * q + ((nl / 128 - n_base / 128) & 1)];
+      const float bsv = ((nl / 128 - n_base / 128) & 1) ? bs1 : bs0;
       v8bf bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) bf[i] = e4m3x8_to_bf16(f[2 * i], f[2 * i + 1]);
@@ -768,7 +778,8 @@ gemm_decode8_kernel(GemmParams p, int rows) {
         v4f pr = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], af[t][i], pr, 0, 0, 0);
-        const float sc = ast[16 * t + r16] * bsv;
+        const int m = 16 * t + r16;
+        const float sc = (CH ? ast[4 * m + q] : ast[64 * q + m]) * bsv;
         acc[j][t][0] = __builtin_fmaf(pr[0], sc, acc[j][t][0]);
         acc[j][t][1] = __builtin_fmaf(pr[1], sc, acc[j][t][1]);
         acc[j][t][2] = __builtin_fmaf(pr[2], sc, acc[j][t][2]);
@@ -1028,10 +1039,15 @@ hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
     // eight-wave kernel: rows per workgroup a multiple of 8, at most 72
     const int rows = 8 * std::min(kDecode8Rows / 8, (groups + cus - 1) / cus);
     const int grid = (p.N + rows - 1) / rows;
-    if (out_f32)
-      gemm_decode8_kernel<MT, true><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
-    else
-      gemm_decode8_kernel<MT, false><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    // a_s as 16 bytes per row and stage: whole stages and 16-byte rows
+    const bool ch = (p.K / 128) % 4 == 0 && ((uintptr_t)p.a_s & 15) == 0;
+    if (out_f32) {
+      if (ch) gemm_decode8_kernel<MT, true, true><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+      else gemm_decode8_kernel<MT, true, false><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    } else {
+      if (ch) gemm_decode8_kernel<MT, false, true><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+      else gemm_decode8_kernel<MT, false, false><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    }
     return hipGetLastError();
   }
   // rows per workgroup: a multiple of 8 that spreads N over the CUs, at most 80
