@@ -834,6 +834,196 @@ gemm_decode8_kernel(GemmParams p, int rows) {
 }
 
 // ----------------------------------------------------------------------------
+// Decode kernel of the BF16 path (W8A16, M <= 32), eight waves.
+// ----------------------------------------------------------------------------
+// The streaming structure of gemm_decode8_kernel with the BF16 path's
+// arithmetic: x is bf16, the weight codes are dequantised in registers with
+// weight_dequant's rounding (float32 product, bf16 RNE) and multiplied on the
+// bf16 MFMA; the block scale is inside the operand, so there is no fold.  A
+// stage holds KPS = 2 K blocks: the weight rows ([2][72][128 B],
+// non-temporal) and the bf16 activation rows ([2][16 MT][256 B]); four
+// stages (three in flight).  The 256-byte x rows put 16-byte chunk c of row
+// r at c ^ (r & 11), which makes the fragment reads conflict-free under the
+// measured bank rule (four cycles of 16 lanes: half-wave x parity of lane
+// bits 2..4).  Wave w computes K block w % 2 for tile set w / 2: tiles {0, 1},
+// {2}, {3} or {4}; the two K-block waves of a set are summed at the end.
+__device__ __forceinline__ int swz256(int r) { return r & 11; }
+
+template <int MT, bool OUT_F32>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+w8a16_decode8_kernel(GemmParams p, int rows) {
+  constexpr int NW = 8, KPS = 2, ST = 4, MR = 16 * MT;
+  constexpr int GRP = kDecode8Rows / 8;                           // 8-row weight groups
+  constexpr int AGRP = MR / 4;                                    // 4-row x groups (1 KB each)
+  constexpr int B_TILE = kDecode8Rows * 128, A_TILE = MR * 256;   // one K block
+  constexpr int B_BYTES = KPS * B_TILE, A_BYTES = KPS * A_TILE;
+  constexpr int STAGE = B_BYTES + A_BYTES;
+  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP, N_REAL = N_B + N_A;
+  constexpr int LPS = (N_REAL + NW - 1) / NW;
+  constexpr int NTW = 2;                                          // tiles per wave (sets 1-3: 1)
+  static_assert(MR <= 32, "shape");
+  static_assert(ST * STAGE + 256 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 256];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int M = p.rows, N = p.N, K = p.K;
+  const int nkb = K / 128, nkc = (nkb + KPS - 1) / KPS;
+  const int n_base = blockIdx.x * rows;
+  const int n_end = min(n_base + rows, N);
+  const int q = wave & 1;                                 // this wave's K block in a stage
+  const int set = wave >> 1;
+  const int jt0 = set == 0 ? 0 : set + 1;                 // first tile of the set
+  const int ntw = set == 0 ? 2 : 1;
+
+  const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)M * K * 2));
+  const v4i b_rsrc = make_rsrc(p.b, (uint32_t)((int64_t)N * K));
+  const int nbn = (N + 127) / 128;
+  typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+  const const_f32_ptr bs_const = (const_f32_ptr)(uintptr_t)p.b_s;
+  const uint32_t smem_lds = lds_addr(smem);
+  const uint32_t dummy_lds = smem_lds + ST * STAGE;
+
+  // DMA instruction u = wave + NW i of a stage:
+  //   u < N_B          weight rows: K block u / GRP, 8-row group u % GRP; lane l
+  //                    takes row l / 8, logical chunk (l % 8) ^ (l / 8)
+  //   u < N_B + N_A    x rows: K block v / AGRP, 4-row group v % AGRP; lane l
+  //                    takes row l / 16, logical chunk (l % 16) ^ swz256(row)
+  //   otherwise        padding (out of range -> zeros into the dummy area)
+  uint32_t voff[LPS], lds_off[LPS], kstep[LPS];
+#pragma unroll
+  for (int i = 0; i < LPS; ++i) {
+    const int u = wave + NW * i;
+    if (u < N_B) {
+      const int kq = u / GRP, grp = u % GRP;
+      const int lchunk = (lane & 7) ^ (lane >> 3);
+      voff[i] = 8 * grp < rows ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq
+                               : 0xF0000000u;
+      lds_off[i] = kq * B_TILE + grp * 1024;
+      kstep[i] = KPS * 128;
+    } else if (u < N_REAL) {
+      const int v = u - N_B, kq = v / AGRP, grp = v % AGRP;
+      const int r = 4 * grp + (lane >> 4);
+      const int lchunk = (lane & 15) ^ swz256(r & 15);
+      voff[i] = (uint32_t)r * (2 * K) + 16 * lchunk + 256 * kq;   // rows >= M read zeros
+      lds_off[i] = B_BYTES + kq * A_TILE + grp * 1024;
+      kstep[i] = KPS * 256;
+    } else {
+      voff[i] = 0xF0000000u;
+      lds_off[i] = 0;
+      kstep[i] = 0;
+    }
+  }
+
+  auto issue = [&](int kc, int st) {
+    const uint32_t base = smem_lds + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int u = wave + NW * i;                        // wave-uniform: scalar branches
+      const uint32_t off = voff[i] + (uint32_t)kc * kstep[i];
+      if (u < N_B) dma_b128_nt(b_rsrc, base + lds_off[i], off);
+      else if (u < N_REAL) dma_b128(a_rsrc, base + lds_off[i], off);
+      else dma_b32(a_rsrc, dummy_lds, 0xF0000000u);
+    }
+  };
+
+  v4f acc[NTW][MT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nkc) issue(s, s);
+
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int st = kc % ST;
+    if (kc + ST - 2 < nkc) wait_vmcnt<(ST - 2) * LPS>();
+    else if (kc + 1 < nkc) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (kc + ST - 1 < nkc) issue(kc + ST - 1, (kc + ST - 1) % ST);
+    const int kbq = kc * KPS + q;
+    if (kbq >= nkb) continue;                            // tail stage: K block past the end
+    const uint8_t* base = smem + st * STAGE;
+    const uint8_t* bt = base + q * B_TILE;
+    const uint8_t* at = base + B_BYTES + q * A_TILE;
+    // the (at most two) weight block scales of this K block (scalar loads;
+    // the second index is clamped: when the rows do not reach a second block
+    // no lane uses it)
+    const int blk0 = n_base / 128, blk1 = min(blk0 + 1, nbn - 1);
+    const float bs0 = bs_const[__builtin_amdgcn_readfirstlane(blk0 * nkb + kbq)];
+    const float bs1 = bs_const[__builtin_amdgcn_readfirstlane(blk1 * nkb + kbq)];
+    // x: lane (r16, g) holds K [32 g + 8 i, +8) of token 16 t + r16 for step i
+    v8bf xf[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint8_t* row = at + (16 * t + r16) * 256;
+      const int sw = swz256(r16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[t][i] = __builtin_bit_cast(v8bf, *(const v4i*)(row + (((4 * g + i) ^ sw) << 4)));
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      if (j >= ntw) break;                                 // wave-uniform
+      const int jt = jt0 + j;
+      const v8i f = lds_frag<0>(bt, 16 * jt + r16, g);     // weight row 16 jt + r16, K [32 g, +32)
+      const int nrow = n_base + 16 * jt + r16;
+      const float sc = ((nrow / 128 - blk0) & 1) ? bs1 : bs0;
+      v8bf bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bf[i] = dequant8_bf16(f[2 * i], f[2 * i + 1], sc);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], xf[t][i], acc[j][t], 0, 0, 0);
+    }
+  }
+
+  // ---- sum the two K-block waves of each tile set, then store
+  constexpr int NV = NTW * MT * 4;
+  float* red = (float*)smem;                             // [NW][NV][64], reused
+  static_assert(NW * NV * 64 * 4 <= ST * STAGE, "reduction area");
+  barrier_lds();
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * NV + (j * MT + t) * 4 + r) * 64 + lane] = acc[j][t][r];
+  barrier_lds();
+  if (q != 0) return;
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    if (j >= ntw) break;
+    const int n = n_base + 16 * (jt0 + j) + 4 * g;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = 16 * t + r16;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[j][t][r] + red[((wave + 1) * NV + (j * MT + t) * 4 + r) * 64 + lane];
+      if (m >= M || n >= n_end) continue;
+      if (OUT_F32) {
+        float* cp = (float*)p.c + (int64_t)m * N + n;
+        if ((N % 4) == 0 && n + 3 < n_end) *(float4*)cp = make_float4(v[0], v[1], v[2], v[3]);
+        else for (int r = 0; r < 4; ++r) if (n + r < n_end) cp[r] = v[r];
+      } else {
+        uint16_t* cp = (uint16_t*)p.c + (int64_t)m * N + n;
+        const uint32_t lo = pack2_bf16(v[0], v[1]), hi = pack2_bf16(v[2], v[3]);
+        if ((N % 4) == 0 && n + 3 < n_end) *(uint2*)cp = make_uint2(lo, hi);
+        else {
+          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+          for (int r = 0; r < 4; ++r) if (n + r < n_end) cp[r] = h[r];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // BF16 path (W8A16): C = x . weight_dequant(W)^T with x bf16, W e4m3 + 128x128
 // block scales ("DeepSeek-V3 Administrator & Developer Guide" 6.3: with
 // gemm_impl "bf16" the FP8 weight is dequantised (8.5.2) and the linear runs
@@ -1173,7 +1363,20 @@ hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, voi
   GemmParams p{};
   p.a = (const uint8_t*)x; p.a_s = nullptr; p.b = (const uint8_t*)w; p.b_s = w_s; p.c = c;
   p.offsets = nullptr; p.rows = (int)M; p.N = (int)N; p.K = (int)K; p.E = 0;
-  if (M <= 32) return run_w8a16<32, 64, 32, 16, 4, 6, 2>(p, out_f32, stream);
+  if (M <= 32) {
+    // eight-wave streaming kernel: rows per workgroup a multiple of 8, at most 72
+    const int cus = device_cus();
+    const int rows = 8 * std::min(kDecode8Rows / 8, ((int)((N + 7) / 8) + cus - 1) / cus);
+    const int grid = (int)((N + rows - 1) / rows);
+    if (M <= 16) {
+      if (out_f32) w8a16_decode8_kernel<1, true><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+      else w8a16_decode8_kernel<1, false><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    } else {
+      if (out_f32) w8a16_decode8_kernel<2, true><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+      else w8a16_decode8_kernel<2, false><<<dim3(grid), dim3(512), 0, stream>>>(p, rows);
+    }
+    return hipGetLastError();
+  }
   if (M <= 64) return run_w8a16<64, 64, 64, 16, 4, 6, 2>(p, out_f32, stream);
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < device_cus()) return run_w8a16<128, 128, 64, 64, 4, 4, 1>(p, out_f32, stream);
