@@ -223,10 +223,41 @@ gemm_tile_kernel(GemmParams p) {
       B = p.b;
       Bs = p.b_s;
     } else {
-      // t = nt * num_m + gm: consecutive workgroups walk the (expert, m-tile)
-      // list for one n tile, so an expert's m tiles run side by side and share
-      // its weight slab.  The list is rebuilt from the device offsets.
-      const int nt = t / p.num_m, gm = t % p.num_m;
+      // The grid is an upper bound on the tile count.  Every workgroup counts
+      // the real (expert, m-tile) pairs from the device offsets, and the real
+      // tiles -- n-minor, so consecutive tiles share an expert's activation
+      // rows -- are dealt to the XCDs as equal contiguous ranges: each XCD
+      // reads a slab of activations once for all its n tiles, and an expert's
+      // weight on the one or two XCDs that hold its m tiles (measured on the
+      // 4096-token MoE: down-projection 1.40-1.49 -> 1.30 ms; an n-major order
+      // made every XCD re-read all activation rows).  The host pads the grid
+      // by 7 so that the eight ranges cover every real tile.
+      int total_m = 0;
+      for (int e0 = 0; e0 < p.E; e0 += 64) {
+        const int ee = e0 + lane;
+        int cnt = 0;
+        if (ee < p.E) {
+          int lo = p.offsets[ee], hi = p.offsets[ee + 1];
+          lo = min(max(lo, 0), p.rows);
+          hi = min(max(hi, lo), p.rows);
+          const int n_rows = hi - lo;
+          cnt = (n_rows > p.moe_lo && n_rows <= p.moe_hi) ? (n_rows + BM - 1) / BM : 0;
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(incl, d);
+          if (lane >= d) incl += v;
+        }
+        total_m += __shfl(incl, 63);
+      }
+      total_m = __builtin_amdgcn_readfirstlane(total_m);
+      const int real = total_m * p.num_n;
+      const int per_xcd = (real + 7) / 8;
+      const int bx = blockIdx.x;
+      const int tt = (bx % 8) * per_xcd + bx / 8;
+      if (bx / 8 >= per_xcd || tt >= real) return;         // no real tile (uniform)
+      const int nt = tt % p.num_n, gm = tt / p.num_n;
       int e = -1, mt = 0;
       {
         int before = 0;                         // m tiles of experts < chunk start
@@ -1329,7 +1360,7 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
     q.num_m = (int)(R / BM + std::min<int64_t>(E, R / (kMoeSplit + 1)));
     q.num_n = (int)((N + BN - 1) / BN);
     if (q.num_m > 0) {
-      const hipError_t err = run_tile<BM, BN, 128, 64, 2, 8, 2, true>(q, out_f32, q.num_m * q.num_n, stream);
+      const hipError_t err = run_tile<BM, BN, 128, 64, 2, 8, 2, true>(q, out_f32, q.num_m * q.num_n + 7, stream);
       if (err != hipSuccess) return err;
     }
   }
@@ -1339,7 +1370,7 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   // sum over experts with <= kMoeSplit rows of ceil(rows / BM) <= E * ceil(kMoeSplit / BM)
   p.num_m = (int)(E * ((kMoeSplit + BM - 1) / BM));
   p.num_n = (int)((N + BN - 1) / BN);
-  return run_tile<BM, BN, 64, 64, 3, 4, 2, true>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<BM, BN, 64, 64, 3, 4, 2, true>(p, out_f32, p.num_m * p.num_n + 7, stream);
 }
 
 template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC>
