@@ -82,7 +82,7 @@ __device__ __forceinline__ void transpose4x4_b8(const uint32_t w[4], uint32_t o[
 }
 
 template <int DN, bool OUT_F32>
-__global__ void __launch_bounds__(256) mla_key_kernel(MlaParams p) {
+__global__ void __launch_bounds__(512) mla_key_kernel(MlaParams p) {
   constexpr int KS = DN / 32;                       // MFMA K steps
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -122,12 +122,18 @@ __global__ void __launch_bounds__(256) mla_key_kernel(MlaParams p) {
     for (int u = 0; u < 4; ++u) wf[s][u] = dequant8_bf16(lo[u], hi[u], sc);
   }
 
+  // The prefetch is unconditional (the last tile reloads itself) and the
+  // stores below are not under a branch: otherwise the compiler's wait count,
+  // merged over both paths, covers the loads just issued and the previous
+  // tile's stores (vmcnt counts both), which serialises the q stream and the
+  // output stream.
+  const int t_last = t_begin + ((t_end - t_begin - 1) / 16) * 16;
   for (int t0 = t_begin; t0 < t_end; t0 += 16) {
     const int t = t0 + j;
     v8bf qf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qcur[s];
-    if (t0 + 16 < t_end) load_q(t0 + 16, qcur);
+    load_q(min(t0 + 16, t_last), qcur);
     v4f acc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -135,9 +141,12 @@ __global__ void __launch_bounds__(256) mla_key_kernel(MlaParams p) {
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(wf[s][u], qf[s], acc[u]);
-    if (t >= t_end) continue;
+    // Rows past the end loaded the last row's q, so their results equal that
+    // row's: they are stored there (the same bytes twice), which keeps the
+    // stores out of a branch.
+    const int ts = min(t, t_end - 1);
     // lane (g, t) owns columns c0 + 16g + e, e = 4r + u
-    const size_t o = ((size_t)t * p.H + h) * p.R + c0 + 16 * g;
+    const size_t o = ((size_t)ts * p.H + h) * p.R + c0 + 16 * g;
     if (OUT_F32) {
       float* out = reinterpret_cast<float*>(p.out) + o;
 #pragma unroll
@@ -163,8 +172,12 @@ __global__ void __launch_bounds__(256) mla_key_kernel(MlaParams p) {
 // (K steps 2s' and 2s'+1 take bytes 0..7 and 8..15) and the 16 bf16 of x at
 // the same c.  Output register r of lane (g', t) is column d0 + 16ct + 4g' + r.
 // ---------------------------------------------------------------------------
+// Two waves per SIMD: with the weight in registers (16 RK VGPRs) a third
+// wave left the compiler too few registers for a tile's x fragments, and it
+// loaded them one at a time with a full wait after each.
 template <int RK, bool OUT_F32>
-__global__ void __launch_bounds__(256) mla_value_kernel(MlaParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_value_kernel(MlaParams p) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int wave = threadIdx.x >> 6;
@@ -205,6 +218,9 @@ __global__ void __launch_bounds__(256) mla_value_kernel(MlaParams p) {
     const int t = t0 + j;
     v8bf xf[RK][2];
     load_x(t0, xf);
+    // all of the tile's x loads are issued before the first MFMA (otherwise
+    // the scheduler pairs each load with its MFMA, two loads in flight)
+    __builtin_amdgcn_sched_barrier(0);
     v4f acc[2][2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) acc[ct][0] = acc[ct][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -214,11 +230,11 @@ __global__ void __launch_bounds__(256) mla_value_kernel(MlaParams p) {
       for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) acc[ct][k] = mfma_bf16(wf[ct][s][k], xf[s][k], acc[ct][k]);
-    if (t >= t_end) continue;
+    const int ts = min(t, t_end - 1);                   // as in the key kernel
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const v4f v = acc[ct][0] + acc[ct][1];
-      const size_t o = ((size_t)t * p.H + h) * p.dv + d0 + 16 * ct + 4 * g;
+      const size_t o = ((size_t)ts * p.H + h) * p.dv + d0 + 16 * ct + 4 * g;
       if (OUT_F32) {
         *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + o) = v;
       } else {
@@ -247,7 +263,11 @@ hipError_t launch_mla_absorb_key(const void* q, int64_t ld_t, int64_t ld_h, cons
   MlaParams p{static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(w), ws, out, (int)T,
               (int)H, (int)dn, (int)dv, (int)R, (int)ld_t, (int)ld_h, 0, 0};
   chunk_tokens(p);
-  const int waves = 4;                                  // 256 latent columns per workgroup
+  // above 64 tokens one workgroup per (head, token chunk) covers up to 512
+  // latent columns, so the chunk's q rows are read once and shared by its
+  // waves (4096 tokens: 265 -> 248 us); at decode sizes four-wave workgroups
+  // spread the weight over more CUs
+  const int waves = T > 64 ? (int)std::min<int64_t>(8, R / 64) : 4;
   const dim3 grid((unsigned)(H * p.n_tch), (unsigned)((R / 64 + waves - 1) / waves));
   const dim3 block(64 * waves);
   if (dn == 128) {
