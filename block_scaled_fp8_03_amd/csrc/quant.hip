@@ -39,12 +39,20 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
                                                                int topk, int64_t nb, int64_t R) {
   const int lane16 = threadIdx.x & 15;
   const int row = threadIdx.x >> 4;
-  const int64_t first = (int64_t)blockIdx.x * kAqBlocksPerWg + row;
+  const int64_t wg_first = (int64_t)blockIdx.x * kAqBlocksPerWg;
+  const int64_t first = wg_first + row;
+  // Loads through a buffer resource over this workgroup's blocks: blocks past
+  // the end read zeros without a branch, so all passes' loads are in flight
+  // together (bounds checks under branches had made the compiler wait for the
+  // first two before issuing the rest).
+  const int64_t wg_blocks = min<int64_t>(nblocks - wg_first, kAqBlocksPerWg);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(x + wg_first * 16), (short)0, (int)(uint32_t)(wg_blocks * 256), 0x00020000);
   uint4 v[kAqPasses];
 #pragma unroll
   for (int u = 0; u < kAqPasses; ++u) {
-    const int64_t b = first + u * (kAqThreads / 16);
-    v[u] = (b < nblocks) ? x[b * 16 + lane16] : make_uint4(0, 0, 0, 0);
+    const uint32_t off = (uint32_t)(((row + u * (kAqThreads / 16)) * 16 + lane16) * 16);
+    v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
   }
 #pragma unroll
   for (int u = 0; u < kAqPasses; ++u) {
@@ -72,12 +80,19 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
         q[b * 16 + lane16] = o;
         if (lane16 == 0) s[b] = sc;
       } else {
+        // the token's routed rows, up to 8 read together, then the stores
         const int64_t t = b / nb, j = b - t * nb;
-        for (int k = 0; k < topk; ++k) {
-          const int64_t r = row_of[t * topk + k];
-          if (r < 0 || r >= R) continue;
-          q[(r * nb + j) * 16 + lane16] = o;
-          if (lane16 == 0) s[r * nb + j] = sc;
+        for (int k0 = 0; k0 < topk; k0 += 8) {
+          int32_t rr[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) rr[k] = row_of[t * topk + min(k0 + k, topk - 1)];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int64_t r = rr[k];
+            if (k0 + k >= topk || r < 0 || r >= R) continue;
+            q[(r * nb + j) * 16 + lane16] = o;
+            if (lane16 == 0) s[r * nb + j] = sc;
+          }
         }
       }
     }
