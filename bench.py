@@ -53,8 +53,8 @@ GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_03_amd", "csrc", "gemm.hip")
 # HBM traffic of one prefill GEMM launch from the rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (scaled by the 1 GiB copy calibration; see profiles/), valid
 # only for the gemm.hip source whose SHA-256 is recorded with it.
-GEMM_TRAFFIC = {"source_sha256": "604281d376a79a2bb4db1c0a1772609704a19cc3d59c30cb446d3d6577f0c931",
-                "fetch_bytes": 837029512, "write_bytes": 152344336}
+GEMM_TRAFFIC = {"source_sha256": "57b55ffd8592c709e89e732375655612404ac6b587f6ea75855726fa5fd068ad",
+                "fetch_bytes": 837024897, "write_bytes": 152430384}
 
 
 def log(*a):
