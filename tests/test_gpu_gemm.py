@@ -92,6 +92,29 @@ def test_gemm_unaligned_scales():
     assert_close(c.float().cpu().numpy(), ref, "gemm unaligned a_s")
 
 
+@pytest.mark.parametrize("M,N,K,unaligned", [
+    (32, 18432, 1536, False),   # eight-wave decode kernel, a_s rows as 16-byte loads
+    (32, 18432, 1536, True),    # the same with a_s 4 bytes past a 16-byte boundary (column loads)
+    (20, 1000, 640, False),     # K/128 = 5: a partial last stage, column loads, 8 rows per workgroup
+    (9, 2050, 7168, True),      # one 16-row activation tile, ragged N, unaligned a_s
+    (32, 130, 512, False),      # two weight blocks in one workgroup, ragged
+])
+def test_gemm_decode_paths(M, N, K, unaligned):
+    """The decode kernel (M <= 32) on each of its code paths, compared in full
+    (outlier activations as in the decode workload)."""
+    a, a_s, b, b_s = rand_operands(M, N, K, 6100 + M + N + K, outliers=True)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    s_dev = to_dev_f32(a_s)
+    if unaligned:
+        buf = torch.zeros(a_s.size + 4, dtype=torch.float32, device=DEV)
+        s_dev = buf[1:1 + a_s.size].view(a_s.shape)
+        s_dev.copy_(torch.from_numpy(a_s).to(DEV))
+        assert (s_dev.data_ptr() % 16) == 4
+    c = fp8bs.fp8_gemm(to_dev_u8(a), s_dev, to_dev_u8(b), to_dev_f32(b_s), torch.float32)
+    torch.cuda.synchronize()
+    assert_close(c.cpu().numpy(), ref, f"decode gemm[{M}x{N}x{K}] unaligned={unaligned}")
+
+
 @pytest.mark.parametrize("M,N,K", SMALL)
 def test_gemm_small(M, N, K):
     a, a_s, b, b_s = rand_operands(M, N, K, 3000 + M * 7 + N)
