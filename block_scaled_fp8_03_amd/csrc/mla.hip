@@ -81,37 +81,61 @@ __device__ __forceinline__ void transpose4x4_b8(const uint32_t w[4], uint32_t o[
   o[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
 }
 
-template <int DN, bool OUT_F32>
-__global__ void __launch_bounds__(512) mla_key_kernel(MlaParams p) {
+// The q tile of 16 tokens (16 rows of DN bf16) is shared by the workgroup's
+// waves through a double-buffered LDS tile, chunk c of row r at c ^ r (as in
+// the value kernel; conflict-free for these reads too): the threads load it
+// one tile ahead into registers (threads past the tile's chunks load
+// duplicates, which write the same bytes), so no wave loads what the others
+// also need.
+template <int DN, int NWK, bool OUT_F32>
+__global__ void __launch_bounds__(64 * NWK) mla_key_kernel(MlaParams p) {
   constexpr int KS = DN / 32;                       // MFMA K steps
+  constexpr int CPR = DN / 8;                       // 16-byte chunks per q row
+  constexpr int ROW_BYTES = CPR * 16;
+  constexpr int TOTAL = 16 * CPR;                   // chunks per tile
+  constexpr int NL = (TOTAL + 64 * NWK - 1) / (64 * NWK);
+  __shared__ __attribute__((aligned(16))) uint8_t qs[2][16 * ROW_BYTES];
+
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int wave = threadIdx.x >> 6;
-  const int c0 = (blockIdx.y * (blockDim.x >> 6) + wave) * 64;
-  if (c0 >= p.R) return;                            // no barriers in this kernel
+  const int c0 = (blockIdx.y * NWK + wave) * 64;
+  const bool active = c0 < p.R;                     // idle waves still load and sync
+  const int cw = active ? c0 : 0;
   const int h = blockIdx.x % p.H;
   const int t_begin = (blockIdx.x / p.H) * p.tch;
   const int t_end = min(p.T, t_begin + p.tch);
+  const int ntiles = (t_end - t_begin + 15) / 16;
   const int row0 = h * (p.dn + p.dv);
 
-  // the first token tile's q is requested before the weight, so both round
-  // trips overlap; inside the loop the next tile's q is requested before the
-  // current tile's MFMAs
-  auto load_q = [&](int t0, v8bf (&qf)[KS]) {
-    const int tl = min(t0 + j, t_end - 1);          // rows past the end load a valid row
-    const uint16_t* q = p.in + (size_t)tl * p.ld_t + (size_t)h * p.ld_h + 8 * g;
+  auto load_tile = [&](int tile, v4u (&qr)[NL]) {
+    const int t0 = t_begin + 16 * tile;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = load_bf16x8(q + 32 * s);
+    for (int i = 0; i < NL; ++i) {
+      const int q = (threadIdx.x + 64 * NWK * i) % TOTAL;
+      const int tl = min(t0 + q / CPR, t_end - 1);  // rows past the end load the last row
+      const uint16_t* src = p.in + (size_t)tl * p.ld_t + (size_t)h * p.ld_h + 8 * (q % CPR);
+      qr[i] = *reinterpret_cast<const v4u*>(src);
+    }
   };
-  v8bf qcur[KS];
-  load_q(t_begin, qcur);
+  auto store_tile = [&](int b, const v4u (&qr)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = (threadIdx.x + 64 * NWK * i) % TOTAL;
+      const int r = q / CPR, c = q % CPR;
+      *reinterpret_cast<v4u*>(&qs[b][r * ROW_BYTES + ((c ^ r) << 4)]) = qr[i];
+    }
+  };
+
+  v4u qr[NL];
+  load_tile(0, qr);
 
   // weight fragments, dequantised once for the whole token chunk
   v8bf wf[KS][4];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const float sc = p.ws[((row0 + 32 * s) >> 7) * (p.R >> 7) + (c0 >> 7)];
-    const uint8_t* base = p.w + (size_t)(row0 + 32 * s + 8 * g) * p.R + c0 + 4 * j;
+    const float sc = p.ws[((row0 + 32 * s) >> 7) * (p.R >> 7) + (cw >> 7)];
+    const uint8_t* base = p.w + (size_t)(row0 + 32 * s + 8 * g) * p.R + cw + 4 * j;
     uint32_t wd[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) wd[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)i * p.R);
@@ -122,83 +146,110 @@ __global__ void __launch_bounds__(512) mla_key_kernel(MlaParams p) {
     for (int u = 0; u < 4; ++u) wf[s][u] = dequant8_bf16(lo[u], hi[u], sc);
   }
 
-  // The prefetch is unconditional (the last tile reloads itself) and the
-  // stores below are not under a branch: otherwise the compiler's wait count,
-  // merged over both paths, covers the loads just issued and the previous
-  // tile's stores (vmcnt counts both), which serialises the q stream and the
-  // output stream.
-  const int t_last = t_begin + ((t_end - t_begin - 1) / 16) * 16;
-  for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-    const int t = t0 + j;
-    v8bf qf[KS];
+  store_tile(0, qr);
+  load_tile(min(1, ntiles - 1), qr);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int b = it & 1;
+    if (active) {
+      const uint8_t* row = qs[b] + j * ROW_BYTES;
+      v4f acc[4];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = qcur[s];
-    load_q(min(t0 + 16, t_last), qcur);
-    v4f acc[4];
+      for (int u = 0; u < 4; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < KS; ++s) {
+        const int c = 4 * s + g;                      // d = 32 s + 8 g .. + 8
+        const v8bf qf = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(row + ((c ^ j) << 4)));
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(wf[s][u], qf, acc[u]);
+      }
+      // Rows past the end computed the last row's q, so their results equal
+      // that row's: they are stored there (the same bytes twice), which keeps
+      // the stores out of a branch.
+      const int ts = min(t_begin + 16 * it + j, t_end - 1);
+      // lane (g, t) owns columns c0 + 16g + e, e = 4r + u
+      const size_t o = ((size_t)ts * p.H + h) * p.R + c0 + 16 * g;
+      if (OUT_F32) {
+        float* out = reinterpret_cast<float*>(p.out) + o;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(wf[s][u], qf[s], acc[u]);
-    // Rows past the end loaded the last row's q, so their results equal that
-    // row's: they are stored there (the same bytes twice), which keeps the
-    // stores out of a branch.
-    const int ts = min(t, t_end - 1);
-    // lane (g, t) owns columns c0 + 16g + e, e = 4r + u
-    const size_t o = ((size_t)ts * p.H + h) * p.R + c0 + 16 * g;
-    if (OUT_F32) {
-      float* out = reinterpret_cast<float*>(p.out) + o;
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<v4f*>(out + 4 * r) = v4f{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      } else {
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<v4f*>(out + 4 * r) = v4f{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-    } else {
-      uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + o;
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const v4u v = {pack2_bf16(acc[0][r], acc[1][r]), pack2_bf16(acc[2][r], acc[3][r]),
-                       pack2_bf16(acc[0][r + 1], acc[1][r + 1]), pack2_bf16(acc[2][r + 1], acc[3][r + 1])};
-        *reinterpret_cast<v4u*>(out + 4 * r) = v;
+        for (int r = 0; r < 4; r += 2) {
+          const v4u v = {pack2_bf16(acc[0][r], acc[1][r]), pack2_bf16(acc[2][r], acc[3][r]),
+                         pack2_bf16(acc[0][r + 1], acc[1][r + 1]), pack2_bf16(acc[2][r + 1], acc[3][r + 1])};
+          *reinterpret_cast<v4u*>(out + 4 * r) = v;
+        }
       }
     }
+    store_tile(b ^ 1, qr);
+    load_tile(min(it + 2, ntiles - 1), qr);
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Value side.  Wave = one head, 32 value columns d0 .. d0+31 (two MFMA row
-// tiles), a chunk of tokens.  The contraction runs along the weight's rows
-// (c), so both operands are read straight: for each 64-wide slice s' of c,
-// lane (j, g) loads the 16 weight bytes [64s' + 16g, +16) of row d0 + 16ct + j
-// (K steps 2s' and 2s'+1 take bytes 0..7 and 8..15) and the 16 bf16 of x at
-// the same c.  Output register r of lane (g', t) is column d0 + 16ct + 4g' + r.
+// tiles), a chunk of tokens; the NWV waves of a workgroup take consecutive
+// 32-column groups of the same head and tokens.  The contraction runs along
+// the weight's rows (c): for each 64-wide slice s' of c, lane (j, g) holds the
+// 16 weight bytes [64s' + 16g, +16) of row d0 + 16ct + j (K steps 2s' and
+// 2s'+1 take bytes 0..7 and 8..15) and the 16 bf16 of x at the same c.
+// Output register r of lane (g', t) is column d0 + 16ct + 4g' + r.
+// The x tile of 16 tokens (16 rows of R bf16) is shared through LDS: each
+// wave loads 16/NWV of its rows into registers one tile ahead and writes them
+// to a double-buffered LDS tile, 16-byte chunk c of row r at c ^ r (found by
+// exhaustive search to keep the fragment reads conflict-free under the
+// measured bank rule); every wave then reads its fragments from LDS (before,
+// each wave loaded the whole tile itself: four times the load instructions).
 // ---------------------------------------------------------------------------
-// Two waves per SIMD: with the weight in registers (16 RK VGPRs) a third
-// wave left the compiler too few registers for a tile's x fragments, and it
-// loaded them one at a time with a full wait after each.
-template <int RK, bool OUT_F32>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int RK, int NWV, bool OUT_F32>
+__global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_value_kernel(MlaParams p) {
+  constexpr int CPR = RK * 8;                       // 16-byte chunks per x row (R / 8)
+  constexpr int ROW_BYTES = CPR * 16;
+  constexpr int TILE_BYTES = 16 * ROW_BYTES;
+  constexpr int NL = 16 * CPR / (64 * NWV);         // 16-byte loads per lane per tile
+  static_assert(16 * CPR % (64 * NWV) == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][TILE_BYTES];
+
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int wave = threadIdx.x >> 6;
-  const int d0 = (blockIdx.y * (blockDim.x >> 6) + wave) * 32;
-  if (d0 >= p.dv) return;                           // no barriers in this kernel
+  const int d0 = (blockIdx.y * NWV + wave) * 32;
+  const bool active = d0 < p.dv;                    // idle waves still load and sync
   const int h = blockIdx.x % p.H;
   const int t_begin = (blockIdx.x / p.H) * p.tch;
   const int t_end = min(p.T, t_begin + p.tch);
-  const int vrow0 = h * (p.dn + p.dv) + p.dn + d0;  // first weight row of the wave
+  const int ntiles = (t_end - t_begin + 15) / 16;
+  const int vrow0 = h * (p.dn + p.dv) + p.dn + (active ? d0 : 0);
 
-  // x is not prefetched across token tiles: with the weight in registers a
-  // second x buffer would leave one wave per SIMD, which measured slower
-  auto load_x = [&](int t0, v8bf (&xf)[RK][2]) {
-    const int tl = min(t0 + j, t_end - 1);          // rows past the end load a valid row
-    const uint16_t* x = p.in + (size_t)tl * p.ld_t + (size_t)h * p.ld_h + 16 * g;
+  // this thread's share of a tile: load q = tid + 64 NWV i, row q / CPR,
+  // chunk q % CPR (rows past the end load the last row)
+  auto load_tile = [&](int tile, v4u (&xr)[NL]) {
+    const int t0 = t_begin + 16 * tile;
 #pragma unroll
-    for (int s = 0; s < RK; ++s) {
-      xf[s][0] = load_bf16x8(x + 64 * s);
-      xf[s][1] = load_bf16x8(x + 64 * s + 8);
+    for (int i = 0; i < NL; ++i) {
+      const int q = threadIdx.x + 64 * NWV * i;
+      const int tl = min(t0 + q / CPR, t_end - 1);
+      const uint16_t* x = p.in + (size_t)tl * p.ld_t + (size_t)h * p.ld_h + 8 * (q % CPR);
+      xr[i] = *reinterpret_cast<const v4u*>(x);
     }
   };
+  auto store_tile = [&](int b, const v4u (&xr)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = threadIdx.x + 64 * NWV * i;
+      const int r = q / CPR, c = q % CPR;
+      *reinterpret_cast<v4u*>(&xs[b][r * ROW_BYTES + ((c ^ r) << 4)]) = xr[i];
+    }
+  };
+
+  v4u xr[NL];
+  load_tile(0, xr);
 
   v8bf wf[2][RK][2];
 #pragma unroll
@@ -214,35 +265,45 @@ mla_value_kernel(MlaParams p) {
     }
   }
 
-  for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-    const int t = t0 + j;
-    v8bf xf[RK][2];
-    load_x(t0, xf);
-    // all of the tile's x loads are issued before the first MFMA (otherwise
-    // the scheduler pairs each load with its MFMA, two loads in flight)
-    __builtin_amdgcn_sched_barrier(0);
-    v4f acc[2][2];
+  store_tile(0, xr);
+  load_tile(min(1, ntiles - 1), xr);
+  __syncthreads();
+
+  for (int i = 0; i < ntiles; ++i) {
+    const int b = i & 1;
+    if (active) {
+      const uint8_t* row = xs[b] + j * ROW_BYTES;
+      v4f acc[2][2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) acc[ct][0] = acc[ct][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ct = 0; ct < 2; ++ct) acc[ct][0] = acc[ct][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < RK; ++s)
+      for (int s = 0; s < RK; ++s)
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+        for (int k = 0; k < 2; ++k) {
+          const int c = 8 * s + 2 * g + k;            // x[16 s' ... ] chunk of this lane
+          const v8bf xf = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(row + ((c ^ j) << 4)));
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) acc[ct][k] = mfma_bf16(wf[ct][s][k], xf[s][k], acc[ct][k]);
-    const int ts = min(t, t_end - 1);                   // as in the key kernel
+          for (int ct = 0; ct < 2; ++ct) acc[ct][k] = mfma_bf16(wf[ct][s][k], xf, acc[ct][k]);
+        }
+      const int ts = min(t_begin + 16 * i + j, t_end - 1);   // as in the key kernel
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const v4f v = acc[ct][0] + acc[ct][1];
-      const size_t o = ((size_t)ts * p.H + h) * p.dv + d0 + 16 * ct + 4 * g;
-      if (OUT_F32) {
-        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + o) = v;
-      } else {
-        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<v2u*>(reinterpret_cast<uint16_t*>(p.out) + o) =
-            v2u{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+      for (int ct = 0; ct < 2; ++ct) {
+        const v4f v = acc[ct][0] + acc[ct][1];
+        const size_t o = ((size_t)ts * p.H + h) * p.dv + d0 + 16 * ct + 4 * g;
+        if (OUT_F32) {
+          *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + o) = v;
+        } else {
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<v2u*>(reinterpret_cast<uint16_t*>(p.out) + o) =
+              v2u{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+        }
       }
     }
+    // the next tile into the other buffer (last read one iteration ago, behind
+    // the barrier that ended it), then the loads of the tile after it
+    store_tile(b ^ 1, xr);
+    load_tile(min(i + 2, ntiles - 1), xr);
+    __syncthreads();
   }
 }
 
@@ -264,19 +325,27 @@ hipError_t launch_mla_absorb_key(const void* q, int64_t ld_t, int64_t ld_h, cons
               (int)H, (int)dn, (int)dv, (int)R, (int)ld_t, (int)ld_h, 0, 0};
   chunk_tokens(p);
   // above 64 tokens one workgroup per (head, token chunk) covers up to 512
-  // latent columns, so the chunk's q rows are read once and shared by its
-  // waves (4096 tokens: 265 -> 248 us); at decode sizes four-wave workgroups
-  // spread the weight over more CUs
-  const int waves = T > 64 ? (int)std::min<int64_t>(8, R / 64) : 4;
+  // latent columns (eight waves), so the chunk's q tile is loaded once for
+  // all of them; at decode sizes four-wave workgroups spread the weight over
+  // more CUs
+  const bool wide = T > 64 && R >= 512;
+  const int waves = wide ? 8 : 4;
   const dim3 grid((unsigned)(H * p.n_tch), (unsigned)((R / 64 + waves - 1) / waves));
   const dim3 block(64 * waves);
-  if (dn == 128) {
-    if (out_f32) hipLaunchKernelGGL((mla_key_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((mla_key_kernel<128, false>), grid, block, 0, stream, p);
-  } else {
-    if (out_f32) hipLaunchKernelGGL((mla_key_kernel<256, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((mla_key_kernel<256, false>), grid, block, 0, stream, p);
+#define FP8BS_MLA_K(DN_)                                                                              \
+  if (wide) {                                                                                       \
+    if (out_f32) hipLaunchKernelGGL((mla_key_kernel<DN_, 8, true>), grid, block, 0, stream, p);     \
+    else hipLaunchKernelGGL((mla_key_kernel<DN_, 8, false>), grid, block, 0, stream, p);            \
+  } else {                                                                                          \
+    if (out_f32) hipLaunchKernelGGL((mla_key_kernel<DN_, 4, true>), grid, block, 0, stream, p);     \
+    else hipLaunchKernelGGL((mla_key_kernel<DN_, 4, false>), grid, block, 0, stream, p);            \
   }
+  if (dn == 128) {
+    FP8BS_MLA_K(128)
+  } else {
+    FP8BS_MLA_K(256)
+  }
+#undef FP8BS_MLA_K
   return hipGetLastError();
 }
 
@@ -288,14 +357,20 @@ hipError_t launch_mla_absorb_value(const void* x, int64_t ld_t, int64_t ld_h, co
   chunk_tokens(p);
   // one wave per workgroup when few tokens (more workgroups to spread the
   // weight over the CUs); four (one head's 128 value columns) otherwise, so
-  // the waves that read the same x rows share a CU
-  const int waves = T <= 64 ? 1 : 4;
+  // the waves that use the same x rows share them through LDS
+  const bool wide = T > 64;
+  const int waves = wide ? 4 : 1;
   const dim3 grid((unsigned)(H * p.n_tch), (unsigned)((dv / 32 + waves - 1) / waves));
   const dim3 block(64 * waves);
-#define FP8BS_MLA_V(RK_)                                                                       \
-  case RK_:                                                                                    \
-    if (out_f32) hipLaunchKernelGGL((mla_value_kernel<RK_, true>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((mla_value_kernel<RK_, false>), grid, block, 0, stream, p);        \
+#define FP8BS_MLA_V(RK_)                                                                            \
+  case RK_:                                                                                         \
+    if (wide) {                                                                                     \
+      if (out_f32) hipLaunchKernelGGL((mla_value_kernel<RK_, 4, true>), grid, block, 0, stream, p);  \
+      else hipLaunchKernelGGL((mla_value_kernel<RK_, 4, false>), grid, block, 0, stream, p);         \
+    } else {                                                                                        \
+      if (out_f32) hipLaunchKernelGGL((mla_value_kernel<RK_, 1, true>), grid, block, 0, stream, p);  \
+      else hipLaunchKernelGGL((mla_value_kernel<RK_, 1, false>), grid, block, 0, stream, p);         \
+    }                                                                                               \
     break;
   switch (R / 64) {
     FP8BS_MLA_V(2)
