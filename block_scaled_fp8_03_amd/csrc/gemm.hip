@@ -117,6 +117,7 @@ struct GemmParams {
   int num_m;              // dense: m tiles; MoE: upper bound on (expert, m-tile) pairs
   int num_n;              // n tiles
   int moe_lo, moe_hi;     // MoE: this launch takes the experts with moe_lo < rows <= moe_hi
+  int n0;                 // dense: first output column of this launch's tiles (a multiple of 128)
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
@@ -219,7 +220,7 @@ gemm_tile_kernel(GemmParams p) {
       const int mt = first_m + in % gsz, nt = in / gsz;
       m_base = mt * BM;
       m_end = p.rows;
-      n_base = nt * BN;
+      n_base = p.n0 + nt * BN;
       B = p.b;
       Bs = p.b_s;
     } else {
@@ -359,6 +360,18 @@ gemm_tile_kernel(GemmParams p) {
 
   const int g = lane >> 4, r16 = lane & 15;
 
+  // Lane-constant parts of the fragment reads.  Fragment rows are 16 apart
+  // and every row block of a tile starts at a multiple of 16, so the swizzle
+  // of row 16 i + r16 is that of r16: each read is one of four lane bases
+  // plus a compile-time offset (the ds_read offset field), with no
+  // per-fragment address arithmetic in the loop.
+  const int fsw = swz<SW>(r16);
+  const uint32_t f_lo = r16 * 128 + (((2 * g) ^ fsw) << 4);
+  const uint32_t f_hi = r16 * 128 + (((2 * g + 1) ^ fsw) << 4);
+  const uint32_t a_lo = wm * WM * 128 + f_lo, a_hi = wm * WM * 128 + f_hi;
+  const uint32_t b_lo = A_BYTES + wn * WN * 128 + f_lo, b_hi = A_BYTES + wn * WN * 128 + f_hi;
+  const uint32_t as_lane = (uint32_t)(wm * WM + r16) * ASC * 4;
+
   // prologue
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
@@ -372,29 +385,38 @@ gemm_tile_kernel(GemmParams p) {
     barrier_lds();
     if (kb + ST - 1 < nkb) issue(kb + ST - 1, (kb + ST - 1) % ST);
 
-    const uint8_t* at = smem + st * STAGE;
-    const uint8_t* bt = at + A_BYTES;
-    const float* ast = ASCH ? (const float*)(smem + ST * STAGE + ((kb / ASC) & 1) * CHUNK_BYTES)
-                            : (const float*)(at + A_BYTES + B_BYTES);
-    const int as_col = ASCH ? kb % ASC : 0;
-    const float bsv = ((const float*)(at + A_BYTES + B_BYTES + AS_BYTES))[wave * 64];
+    const uint8_t* sbase = smem + st * STAGE;
+    // fragment rows 16 i .. 16 i + 15 from the lane bases (lo, hi)
+    auto frag = [&](uint32_t lo, uint32_t hi, int i) {
+      const uint4 x = *(const uint4*)(sbase + lo + i * 2048);
+      const uint4 y = *(const uint4*)(sbase + hi + i * 2048);
+      v8i v;
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+      return v;
+    };
+    // this lane's activation scale of fragment row block t: a_s[row][as_col]
+    // of the [BM][ASC] chunk (or the stage's [BM] column when ASC = 1)
+    const uint8_t* asb = (ASCH ? smem + ST * STAGE + ((kb / ASC) & 1) * CHUNK_BYTES
+                               : sbase + A_BYTES + B_BYTES) + as_lane + (ASCH ? (kb % ASC) * 4 : 0);
+    const float bsv = ((const float*)(sbase + A_BYTES + B_BYTES + AS_BYTES))[wave * 64];
     v8i bf[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) bf[j] = lds_frag<SW>(bt, wn * WN + 16 * j + r16, g);
+    for (int j = 0; j < NT; ++j) bf[j] = frag(b_lo, b_hi, j);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const int ml = wm * WM + 16 * t + r16;
-      const v8i af = lds_frag<SW>(at, ml, g);
+      const v8i af = frag(a_lo, a_hi, t);
+      const float as_t = *(const float*)(asb + t * 16 * ASC * 4);
       if (E8) {
         // E8M0 exponents: the biased exponent field of each power-of-two scale
-        const int ea = (int)(f32_bits(ast[ml * ASC + as_col]) >> 23);
+        const int ea = (int)(f32_bits(as_t) >> 23);
         const int eb = (int)(f32_bits(bsv) >> 23);
 #pragma unroll
         for (int j = 0; j < NT; ++j)
           acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[j][t], 0, 0, 0, eb, 0, ea);
         continue;
       }
-      const float sc = ast[ml * ASC + as_col] * bsv;
+      const float sc = as_t * bsv;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const v4f pr = mfma_k128(bf[j], af);
@@ -1141,6 +1163,12 @@ w8a16_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[j][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   const int g = lane >> 4, r16 = lane & 15;
+  // lane bases of the fragment reads (row blocks start at multiples of 16,
+  // so both swizzles depend on r16 only): x chunk 2g + s of row 16t + r16 at
+  // xa[s] + 2048 t, the weight chunk g of row 16j + r16 at wb + 1024 j
+  const uint32_t xa0 = (uint32_t)(wm * WM + r16) * 128 + (((2 * g) ^ swz<2>(r16)) << 4);
+  const uint32_t xa1 = (uint32_t)(wm * WM + r16) * 128 + (((2 * g + 1) ^ swz<2>(r16)) << 4);
+  const uint32_t wb = A_BYTES + (uint32_t)(wn * WN + r16) * 64 + ((g ^ swz64(r16)) << 4);
 
 #pragma unroll
   for (int s0 = 0; s0 < ST - 1; ++s0)
@@ -1154,23 +1182,19 @@ w8a16_tile_kernel(GemmParams p) {
     if (ks + ST - 1 < nks) issue(ks + ST - 1, (ks + ST - 1) % ST);
 
     const uint8_t* at = smem + st * STAGE;
-    const uint8_t* bt = at + A_BYTES;
     const float bsv = ((const float*)(at + A_BYTES + B_BYTES))[wave * 64];
     v8bf bf[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int row = wn * WN + 16 * j + r16;
-      const uint4 w = *(const uint4*)(bt + row * 64 + ((g ^ swz64(row)) << 4));
+      const uint4 w = *(const uint4*)(at + wb + j * 1024);
       bf[j][0] = dequant8_bf16(w.x, w.y, bsv);
       bf[j][1] = dequant8_bf16(w.z, w.w, bsv);
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const int ml = wm * WM + 16 * t + r16;
-      const int sw = swz<2>(ml);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const v8bf af = __builtin_bit_cast(v8bf, *(const uint4*)(at + ml * 128 + (((2 * g + s) ^ sw) << 4)));
+        const v8bf af = __builtin_bit_cast(v8bf, *(const uint4*)(at + (s ? xa1 : xa0) + t * 2048));
 #pragma unroll
         for (int j = 0; j < NT; ++j)
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j][s], af, acc[j][t], 0, 0, 0);
@@ -1283,6 +1307,12 @@ hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
 
 }  // namespace
 
+// Time of a 128 x 256 tile relative to a 256 x 256 tile of the same K.
+#ifndef FP8BS_TAIL_COST
+#define FP8BS_TAIL_COST 0.75
+#endif
+constexpr double kTailCost = FP8BS_TAIL_COST;
+
 template <bool E8>
 hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
                       int64_t M, int64_t N, int64_t K, bool out_f32, hipStream_t stream) {
@@ -1316,6 +1346,32 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   }
   p.num_m = (int)((M + BM - 1) / BM);
   p.num_n = (int)((N + BN - 1) / BN);
+  // One workgroup per CU, so a launch takes ceil(tiles / CUs) rounds of
+  // equal tiles.  When the last round would be partly empty, the columns
+  // past the last full round run as a second launch of 128 x 256 tiles
+  // (twice as many, each faster than a 256 x 256 tile), if the model
+  // full rounds + tail rounds x kTailCost beats one more full round.
+  const int64_t T = (int64_t)p.num_m * p.num_n;
+  const int64_t full = T / cus * cus;
+  if (BM == 256 && BN == 256 && T > cus && full != T && full % p.num_m == 0) {
+    const int n_main = (int)(full / p.num_m);
+    const int64_t tail_cols = N - (int64_t)n_main * BN;
+    const int64_t tail_tiles = ((M + 127) / 128) * ((tail_cols + 255) / 256);
+    const double split_cost = (double)(full / cus) + (double)((tail_tiles + cus - 1) / cus) * kTailCost;
+    if (split_cost < (double)((T + cus - 1) / cus)) {
+      p.num_n = n_main;
+      hipError_t e = run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, (int)full, stream);
+      if (e != hipSuccess) return e;
+      GemmParams q = p;
+      q.n0 = n_main * BN;
+      q.num_m = (int)((M + 127) / 128);
+      q.num_n = (int)((tail_cols + 255) / 256);
+      // three stages (a_s per stage, which leaves room for the third): a
+      // tile this small waits on the DMA round trip with only two
+      launch_tile<128, 256, 64, 64, 3, 8, 2, false, false, 1, E8>(q, out_f32, q.num_m * q.num_n, stream);
+      return hipGetLastError();
+    }
+  }
   return run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
 }
 

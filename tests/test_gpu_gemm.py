@@ -158,6 +158,29 @@ def test_gemm_extreme_scales_tile():
     assert np.all(err <= bound), (err / bound).max()
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (4096, 18432, 256),   # the prefill tile grid: 1024 tiles in full rounds + a 2048-column tail
+    (4000, 18000, 512),   # ragged M and N, tail of 1616 columns, a_s in chunks
+])
+def test_gemm_tail_split(M, N, K):
+    """Tile grids that leave the last round of 256 x 256 tiles partly empty run
+    the columns past the full rounds as a second launch of 128 x 256 tiles;
+    compared in full (float32 scales, then power-of-two scales on the scaled
+    MFMA), the boundary columns included."""
+    a, a_s, b, b_s = rand_operands(M, N, K, 5100 + M + N + K)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    assert_close(run_gemm(a, a_s, b, b_s, torch.float32), ref, f"gemm[{M}x{N}x{K}] f32 split")
+    assert_close(run_gemm(a, a_s, b, b_s, torch.bfloat16), ref, f"gemm[{M}x{N}x{K}] bf16 split")
+    x = inputs.normal_bf16((M, K), 1.0, 5200 + M)
+    w = inputs.normal_bf16((N, K), 0.02, 5201 + M)
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), oracle.FMT_UE8M0)
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w), oracle.FMT_UE8M0)
+    ref = oracle.gemm(a, a_s, b, b_s)
+    c = fp8bs.fp8_gemm_ue8m0(to_dev_u8(a), to_dev_f32(a_s), to_dev_u8(b), to_dev_f32(b_s), torch.float32)
+    torch.cuda.synchronize()
+    assert_close(c.cpu().numpy(), ref, f"gemm ue8m0[{M}x{N}x{K}] f32 split")
+
+
 def test_tiny_linear_end_to_end():
     """The tiny FP8 linear: x bf16 [16, 256] ~ N(0,1), W [256, 256] ~ N(0, 0.02)
     quantised to 2x2 blocks; act_quant on the GPU then the GEMM."""
