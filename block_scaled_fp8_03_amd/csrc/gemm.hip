@@ -383,7 +383,6 @@ gemm_tile_kernel(GemmParams p) {
     if (kb + ST - 2 < nkb) wait_vmcnt<(ST - 2) * LPS>();
     else wait_vmcnt<0>();
     barrier_lds();
-    if (kb + ST - 1 < nkb) issue(kb + ST - 1, (kb + ST - 1) % ST);
 
     const uint8_t* sbase = smem + st * STAGE;
     // fragment rows 16 i .. 16 i + 15 from the lane bases (lo, hi)
@@ -403,9 +402,15 @@ gemm_tile_kernel(GemmParams p) {
     v8i bf[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) bf[j] = frag(b_lo, b_hi, j);
+    const v8i af0 = frag(a_lo, a_hi, 0);
+    // The next stage's DMA goes out after the operand reads of this K block's
+    // first MFMAs, so those reads do not queue behind the workgroup's burst of
+    // DMA instructions.  It fills the other stage (and possibly the other a_s
+    // chunk buffer), which every wave finished reading before the barrier.
+    if (kb + ST - 1 < nkb) issue(kb + ST - 1, (kb + ST - 1) % ST);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const v8i af = frag(a_lo, a_hi, t);
+      const v8i af = t == 0 ? af0 : frag(a_lo, a_hi, t);
       const float as_t = *(const float*)(asb + t * 16 * ASC * 4);
       if (E8) {
         // E8M0 exponents: the biased exponent field of each power-of-two scale
