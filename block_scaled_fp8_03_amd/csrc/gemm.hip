@@ -1184,22 +1184,28 @@ w8a16_tile_kernel(GemmParams p) {
     if (ks + ST - 2 < nks) wait_vmcnt<(ST - 2) * LPS>();
     else wait_vmcnt<0>();
     barrier_lds();
-    if (ks + ST - 1 < nks) issue(ks + ST - 1, (ks + ST - 1) % ST);
 
     const uint8_t* at = smem + st * STAGE;
     const float bsv = ((const float*)(at + A_BYTES + B_BYTES))[wave * 64];
+    uint4 wr[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) wr[j] = *(const uint4*)(at + wb + j * 1024);
+    const uint4 x00 = *(const uint4*)(at + xa0);
+    // the next stage's DMA after the first operand reads (as in the FP8 tile
+    // kernel); it fills a stage every wave finished reading before the barrier
+    if (ks + ST - 1 < nks) issue(ks + ST - 1, (ks + ST - 1) % ST);
     v8bf bf[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const uint4 w = *(const uint4*)(at + wb + j * 1024);
-      bf[j][0] = dequant8_bf16(w.x, w.y, bsv);
-      bf[j][1] = dequant8_bf16(w.z, w.w, bsv);
+      bf[j][0] = dequant8_bf16(wr[j].x, wr[j].y, bsv);
+      bf[j][1] = dequant8_bf16(wr[j].z, wr[j].w, bsv);
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const v8bf af = __builtin_bit_cast(v8bf, *(const uint4*)(at + (s ? xa1 : xa0) + t * 2048));
+        const v8bf af = __builtin_bit_cast(
+            v8bf, (t == 0 && s == 0) ? x00 : *(const uint4*)(at + (s ? xa1 : xa0) + t * 2048));
 #pragma unroll
         for (int j = 0; j < NT; ++j)
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j][s], af, acc[j][t], 0, 0, 0);
