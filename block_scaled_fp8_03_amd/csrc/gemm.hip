@@ -19,6 +19,7 @@
 // result lane l, register r is D[4 (l / 16) + r][l % 16].
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "device_common.h"
 #include "launch.h"
@@ -1399,6 +1400,42 @@ hipError_t launch_gemm_ue8m0(const void* a, const float* a_s, const void* b, con
   return dense_gemm<true>(a, a_s, b, b_s, c, M, N, K, out_f32, stream);
 }
 
+namespace {
+
+// A second stream and two events per device, for a launch made of two
+// independent kernels that should share the CUs: the caller's stream records
+// `fork`, the side stream waits on it and takes one kernel and records
+// `join`, and the caller's stream takes the other kernel and waits on
+// `join` -- so on the caller's stream the pair is ordered like one launch
+// (and a stream capture records it as a fork and a join).  Created on first
+// use and kept for the process, at the default priority; the mutex keeps the
+// record/wait pairs of concurrent host threads from interleaving.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+
+SideStream* side_stream() {
+  static SideStream table[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& x = table[dev];
+  std::lock_guard<std::mutex> g(x.mu);
+  if (!x.s && !x.failed) {
+    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
+      x.failed = true;              // fall back to one stream from now on
+      (void)hipGetLastError();
+    }
+  }
+  return x.failed ? nullptr : &x;
+}
+
+}  // namespace
+
 hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
                            const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N,
                            int64_t K, bool out_f32, hipStream_t stream) {
@@ -1417,6 +1454,22 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
 #define FP8BS_MOE_SPLIT 64
 #endif
   constexpr int kMoeSplit = FP8BS_MOE_SPLIT;
+  // The two classes run side by side (the small experts on the side stream):
+  // under skewed routing one is bound by the matrix cores and the other by
+  // HBM, and each grid's last round of workgroups is only partly full, so
+  // the CUs are better used when the two grids share them than one after the
+  // other.
+  SideStream* ss = side_stream();
+  std::unique_lock<std::mutex> lock;
+  hipStream_t small_stream = stream;
+  if (ss) {
+    lock = std::unique_lock<std::mutex>(ss->mu);
+    hipError_t e = hipEventRecord(ss->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return e;
+    small_stream = ss->s;
+  }
+  hipError_t err = hipSuccess;
   {
     constexpr int BM = 256, BN = 256;
     GemmParams q = p;
@@ -1426,18 +1479,26 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
     //   <= R / BM + (number of such experts) <= R / BM + R / (kMoeSplit + 1)
     q.num_m = (int)(R / BM + std::min<int64_t>(E, R / (kMoeSplit + 1)));
     q.num_n = (int)((N + BN - 1) / BN);
-    if (q.num_m > 0) {
-      const hipError_t err = run_tile<BM, BN, 128, 64, 2, 8, 2, true>(q, out_f32, q.num_m * q.num_n + 7, stream);
-      if (err != hipSuccess) return err;
-    }
+    if (q.num_m > 0) err = run_tile<BM, BN, 128, 64, 2, 8, 2, true>(q, out_f32, q.num_m * q.num_n + 7, stream);
   }
-  constexpr int BM = 64, BN = 256;
-  p.moe_lo = 0;
-  p.moe_hi = kMoeSplit;
-  // sum over experts with <= kMoeSplit rows of ceil(rows / BM) <= E * ceil(kMoeSplit / BM)
-  p.num_m = (int)(E * ((kMoeSplit + BM - 1) / BM));
-  p.num_n = (int)((N + BN - 1) / BN);
-  return run_tile<BM, BN, 64, 64, 3, 4, 2, true>(p, out_f32, p.num_m * p.num_n + 7, stream);
+  if (err == hipSuccess) {
+    constexpr int BM = 64, BN = 256;
+    GemmParams q = p;
+    q.moe_lo = 0;
+    q.moe_hi = kMoeSplit;
+    // sum over experts with <= kMoeSplit rows of ceil(rows / BM) <= E * ceil(kMoeSplit / BM)
+    q.num_m = (int)(E * ((kMoeSplit + BM - 1) / BM));
+    q.num_n = (int)((N + BN - 1) / BN);
+    err = run_tile<BM, BN, 64, 64, 3, 4, 2, true>(q, out_f32, q.num_m * q.num_n + 7, small_stream);
+  }
+  if (ss) {
+    // join even after a failed launch, so the side stream never runs ahead
+    // of later work on the caller's stream
+    hipError_t e = hipEventRecord(ss->join, ss->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
+    if (err == hipSuccess) err = e;
+  }
+  return err;
 }
 
 template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC>

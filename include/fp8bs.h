@@ -145,10 +145,14 @@ int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
  *                 left untouched
  *   R, E >= 0 (either 0 = no-op), N >= 0, K >= 128 with K % 128 == 0;
  *   (R + 256) * K < 2^32 and (N + 256) * K < 2^32.
- * Runs as two launches on `stream`: experts with more than 64 rows on the
- * 256 x 256 tiles of fp8bs_gemm, the others on 64 x 256 tiles.  Both grids
- * are sized on the host from R and E alone (each finds its experts from the
- * device offsets); experts with no rows cost (almost) nothing.
+ * Runs as two launches: experts with more than 64 rows on the 256 x 256
+ * tiles of fp8bs_gemm (on `stream`), the others on 64 x 256 tiles, on a
+ * second stream the library keeps per device (default priority) that waits
+ * for `stream` before it starts, and that `stream` waits for afterwards: on
+ * `stream` the call is ordered like a single launch, and a stream capture of
+ * `stream` records it as a fork and a join.  Both grids are sized on the host
+ * from R and E alone (each finds its experts from the device offsets);
+ * experts with no rows cost (almost) nothing.
  */
 int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
                    const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N, int64_t K,
