@@ -58,8 +58,8 @@ GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_03_amd", "csrc", "gemm.hip")
 # FETCH_SIZE and WRITE_SIZE runs (scaled by the 1 GiB copy calibration; see
 # profiles/), valid only for the gemm.hip source whose SHA-256 is recorded
 # with it.
-GEMM_TRAFFIC = {"source_sha256": "15c1ae564fa7918fcb99057d6cc02e237c9ee1a42f856275873696025754b781",
-                "fetch_bytes": 864587436, "write_bytes": 151999744}
+GEMM_TRAFFIC = {"source_sha256": "14e18a48645836ce23504a4f33b908b26fff19ee9e8accd0728009256bf494f1",
+                "fetch_bytes": 864490701, "write_bytes": 151964877}
 
 
 def log(*a):
