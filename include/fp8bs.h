@@ -11,8 +11,11 @@
  *   - Block size is 128 everywhere: activations carry one float32 scale per
  *     1 x 128 block along K, weights one per 128 x 128 block.  A scale is the
  *     dequantisation multiplier: real value = decode(code) * scale.
- *   - The caller owns all memory.  The library never allocates or frees,
- *     keeps no global state, and is safe to call from several host threads.
+ *   - The caller owns all memory.  The library never allocates or frees
+ *     device memory.  Its only process-wide state is a per-device cache of
+ *     the compute-unit count and, for fp8bs_moe_gemm, one extra stream and
+ *     two events per device, created on first use (under a mutex) and kept
+ *     until the process ends.  It is safe to call from several host threads.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream) on the
  *     current HIP device; all pointers must be device (or managed) memory of
  *     that device.
