@@ -87,6 +87,23 @@ __device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, uint32_t voff) {
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
+// The same two loads with a wave-uniform byte offset in the instruction's
+// scalar offset field: the K position of a tile's loads advances in an SGPR
+// instead of one VALU add per load and K block.  Every such offset stays
+// inside the row that `voff` addresses (or `voff` alone is already past the
+// end of the buffer), so the range check zero-fills exactly the loads it did
+// without the scalar offset.
+__device__ __forceinline__ void dma_b128s(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32s(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -335,22 +352,22 @@ gemm_tile_kernel(GemmParams p) {
     const uint32_t koff = (uint32_t)kb * 128;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-      dma_b128(a_rsrc, base + i * NW * 1024, a_voff + i * rowstep + koff);
+      dma_b128s(a_rsrc, base + i * NW * 1024, a_voff + i * rowstep, koff);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-      dma_b128(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep + koff);
+      dma_b128s(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
     if (ASCH) {
       if (kb % ASC == 0)
-        dma_b128(as_rsrc, chunk_lds + ((kb / ASC) & 1) * CHUNK_BYTES, asc_voff + kb * 4);
+        dma_b128s(as_rsrc, chunk_lds + ((kb / ASC) & 1) * CHUNK_BYTES, asc_voff, (uint32_t)kb * 4);
       else if (ST > 2)
         dma_b32(as_rsrc, dummy_lds, 0xF0000000u);
     } else {
       // a_s: thread t fetches row t % BM into slot t (slots >= BM hold copies)
-      dma_b32(as_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, as_voff + kb * 4);
+      dma_b32s(as_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, as_voff, (uint32_t)kb * 4);
     }
     // every lane of the wave fetches the same b_s value of its weight block
-    dma_b32(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + AS_BYTES + wave * 256,
-            bs_voff + kb * 4);
+    dma_b32s(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + AS_BYTES + wave * 256,
+             bs_voff, (uint32_t)kb * 4);
   };
 
   v4f acc[NT][MT];
@@ -1156,11 +1173,11 @@ w8a16_tile_kernel(GemmParams p) {
     const uint32_t base = smem_lds + st * STAGE + wave * 1024;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-      dma_b128(a_rsrc, base + i * NW * 1024, a_voff + i * a_step + (uint32_t)ks * 128);
+      dma_b128s(a_rsrc, base + i * NW * 1024, a_voff + i * a_step, (uint32_t)ks * 128);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-      dma_b128(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * b_step + (uint32_t)ks * 64);
-    dma_b32(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, bs_voff + (ks / 2) * 4);
+      dma_b128s(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * b_step, (uint32_t)ks * 64);
+    dma_b32s(bs_rsrc, smem_lds + st * STAGE + A_BYTES + B_BYTES + wave * 256, bs_voff, (uint32_t)(ks / 2) * 4);
   };
 
   v4f acc[NT][MT];
