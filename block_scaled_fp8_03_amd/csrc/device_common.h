@@ -19,6 +19,29 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
 
+// Streaming (read-once / write-once) memory accesses: the non-temporal hint
+// keeps data that is not reused from displacing what is.  Measured (same-box
+// A/B, inputs larger than the caches): act_quant 4096 x 18432 42.3 -> 39.5 us,
+// MoE quant_scatter 67.9 -> 62.0 us, MoE combine 101.9 -> 89.2 us; on
+// weight_dequant it cost 2% and is not used there.  kNonTemporal is the
+// cache-policy operand of the raw buffer load builtins (the `nt` bit on
+// gfx950).
+constexpr int kNonTemporal = 2;
+template <typename T>
+__device__ __forceinline__ void store_nt(T* p, const T& v);
+template <>
+__device__ __forceinline__ void store_nt<uint2>(uint2* p, const uint2& v) {
+  __builtin_nontemporal_store(v.x, &((uint32_t*)p)[0]);
+  __builtin_nontemporal_store(v.y, &((uint32_t*)p)[1]);
+}
+template <>
+__device__ __forceinline__ void store_nt<uint4>(uint4* p, const uint4& v) {
+  __builtin_nontemporal_store(v.x, &((uint32_t*)p)[0]);
+  __builtin_nontemporal_store(v.y, &((uint32_t*)p)[1]);
+  __builtin_nontemporal_store(v.z, &((uint32_t*)p)[2]);
+  __builtin_nontemporal_store(v.w, &((uint32_t*)p)[3]);
+}
+
 // Two bf16 values packed in one dword -> two floats (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return bits_f32(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return bits_f32(w & 0xFFFF0000u); }

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kCombineThreads) void moe_combine_vec_kernel(
   for (int k = 0; k < KMAX; ++k) {
     const bool ok = k < topk && r[k] >= 0 && r[k] < R;
     const uint32_t off = ok ? (uint32_t)(((int64_t)r[k] * nv + v) * 16) : 0xF0000000u;
-    o[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    o[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kNonTemporal);
     if (!ok) wk[k] = 0.0f;
   }
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -322,12 +322,12 @@ __global__ __launch_bounds__(kCombineThreads) void moe_combine_vec_kernel(
     }
   }
   if (OUT_F32) {
-    float4* yp = (float4*)y + 2 * i;
-    yp[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    yp[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    uint4* yp = (uint4*)y + 2 * i;
+    store_nt(yp, make_uint4(f32_bits(acc[0]), f32_bits(acc[1]), f32_bits(acc[2]), f32_bits(acc[3])));
+    store_nt(yp + 1, make_uint4(f32_bits(acc[4]), f32_bits(acc[5]), f32_bits(acc[6]), f32_bits(acc[7])));
   } else {
-    ((uint4*)y)[i] = make_uint4(pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
-                                pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7]));
+    store_nt((uint4*)y + i, make_uint4(pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
+                                       pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7])));
   }
 }
 

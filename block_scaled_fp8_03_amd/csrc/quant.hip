@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
 #pragma unroll
   for (int u = 0; u < kAqPasses; ++u) {
     const uint32_t off = (uint32_t)(((row + u * (kAqThreads / 16)) * 16 + lane16) * 16);
-    v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kNonTemporal));
   }
 #pragma unroll
   for (int u = 0; u < kAqPasses; ++u) {
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
                      div_markstein(f[6], sc, r), div_markstein(f[7], sc, r));
     if (b < nblocks) {
       if (!SCATTER) {
-        q[b * 16 + lane16] = o;
+        store_nt(q + b * 16 + lane16, o);
         if (lane16 == 0) s[b] = sc;
       } else {
         // the token's routed rows, up to 8 read together, then the stores
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
           for (int k = 0; k < 8; ++k) {
             const int64_t r = rr[k];
             if (k0 + k >= topk || r < 0 || r >= R) continue;
-            q[(r * nb + j) * 16 + lane16] = o;
+            store_nt(q + (r * nb + j) * 16 + lane16, o);
             if (lane16 == 0) s[r * nb + j] = sc;
           }
         }
