@@ -98,6 +98,11 @@ __device__ __forceinline__ void dma_b128s(v4i rsrc, uint32_t lds, uint32_t voff,
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
+__device__ __forceinline__ void dma_b128s_nt(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
 __device__ __forceinline__ void dma_b32s(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
@@ -354,8 +359,14 @@ gemm_tile_kernel(GemmParams p) {
     for (int i = 0; i < A_LOADS; ++i)
       dma_b128s(a_rsrc, base + i * NW * 1024, a_voff + i * rowstep, koff);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      dma_b128s(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
+    for (int i = 0; i < B_LOADS; ++i) {
+      // The small-expert MoE tiles (at most 64 rows per expert, one m tile)
+      // read each expert's weight exactly once: non-temporal DMA (measured on
+      // the 4096-token MoE: up 1062 -> 1030 us, down 1169 -> 1124 us; the
+      // same hint on the 256-row tiles of single-tile experts did not help).
+      if (MOE && BM == 64) dma_b128s_nt(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
+      else dma_b128s(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
+    }
     if (ASCH) {
       if (kb % ASC == 0)
         dma_b128s(as_rsrc, chunk_lds + ((kb / ASC) & 1) * CHUNK_BYTES, asc_voff, (uint32_t)kb * 4);
