@@ -23,9 +23,11 @@ __device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f
 // keeps data that is not reused from displacing what is.  Measured (same-box
 // A/B, inputs larger than the caches): act_quant 4096 x 18432 42.3 -> 39.5 us,
 // MoE quant_scatter 67.9 -> 62.0 us, MoE combine 101.9 -> 89.2 us; on
-// weight_dequant it cost 2% and is not used there.  kNonTemporal is the
-// cache-policy operand of the raw buffer load builtins (the `nt` bit on
-// gfx950).
+// weight_dequant it cost 2% and is not used there.  The stores pay only where
+// a wave writes whole cache lines: on the GEMM and MLA epilogues, whose lanes
+// write 8-16 bytes at a row stride, they were several times slower.
+// kNonTemporal is the cache-policy operand of the raw buffer load builtins
+// (the `nt` bit on gfx950).
 constexpr int kNonTemporal = 2;
 template <typename T>
 __device__ __forceinline__ void store_nt(T* p, const T& v);

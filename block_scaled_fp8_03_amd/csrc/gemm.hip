@@ -87,8 +87,8 @@ __device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, uint32_t voff) {
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
-// The same two loads with a wave-uniform byte offset in the instruction's
-// scalar offset field: the K position of a tile's loads advances in an SGPR
+// The loads above with a wave-uniform byte offset in the instruction's
+// scalar offset field (and a non-temporal form of the 16-byte one): the K position of a tile's loads advances in an SGPR
 // instead of one VALU add per load and K block.  Every such offset stays
 // inside the row that `voff` addresses (or `voff` alone is already past the
 // end of the buffer), so the range check zero-fills exactly the loads it did
