@@ -19,13 +19,14 @@ namespace fp8bs {
 // The input is a flat sequence of 128-element blocks (K % 128 == 0, row-major),
 // and block b's scale lives at s[b] ([M, K/128] row-major is that order).
 // A 16-lane row handles one block: lane i holds elements 8i .. 8i+7 (16 bytes
-// of bf16) and writes their 8 e4m3 bytes.  A 512-thread workgroup covers 32
-// blocks per pass and kAqPasses = 2 passes, all loads issued before any use
-// (measured against 256 x 4, 256 x 2, 512 x 1, 512 x 4, 768 x 2 and 1024 x 1 on
-// 4096 x 7168 and 4096 x 18432: the best or tied on every case; 16.7 -> 15.8 us
-// on 4096 x 7168 when x is cache-resident).
+// of bf16) and writes their 8 e4m3 bytes.  A 256-thread workgroup covers 16
+// blocks per pass and kAqPasses = 2 passes, all loads issued before any use.
+// With the non-temporal loads and stores this shape measured best against
+// 512 x 2, 1024 x 2, 512 x 4, 256 x 4 and 512 x 1 on every workload (same box:
+// 4096 x 18432 39.4 -> 38.3 us, 32768 x 2048 35.0 -> 34.1 us, 1024 x 7168 ue8m0
+// 6.5 -> 6.0 us, 4096 x 7168 cache-resident 16.3 -> 15.8 us, against 512 x 2).
 #ifndef FP8BS_AQ_THREADS
-#define FP8BS_AQ_THREADS 512
+#define FP8BS_AQ_THREADS 256
 #endif
 #ifndef FP8BS_AQ_PASSES
 #define FP8BS_AQ_PASSES 2
