@@ -307,10 +307,21 @@ mla_value_kernel(MlaParams p) {
   }
 }
 
-// Token chunking: at most 256 tokens per workgroup, evenly split, a multiple
-// of 16.
+// Token chunking, evenly split, a multiple of 16: the largest chunk of 1024,
+// 512 or 256 tokens that still gives at least 512 workgroups (two per CU)
+// over the heads, else 256.  Longer chunks load each head's weight fewer
+// times (measured, 128 heads: 4096 tokens key 167.3 -> 157.5 us and value
+// 131.4 -> 127.4 us with 1024-token chunks against 256; 2048 tokens value
+// 64.6 -> 62.0 us with 512), but a grid below two workgroups per CU lost
+// more than that (1000 tokens in 1024-token chunks: 30 -> 57 us).
 void chunk_tokens(MlaParams& p) {
-  p.n_tch = std::max(1, (p.T + 255) / 256);
+  int cap = 256;
+  for (int c : {1024, 512})
+    if ((int64_t)p.H * ((p.T + c - 1) / c) >= 512) {
+      cap = c;
+      break;
+    }
+  p.n_tch = std::max(1, (p.T + cap - 1) / cap);
   const int per = (p.T + p.n_tch - 1) / p.n_tch;
   p.tch = (per + 15) / 16 * 16;
   p.n_tch = (p.T + p.tch - 1) / p.tch;
