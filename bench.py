@@ -48,17 +48,17 @@ ROTATE_FOOTPRINT = 2 * MALL_BYTES
 
 # The prefill GEMM call is two kernels on one stream: 1024 tiles of 256x256
 # (128x64 per wave, 2 LDS stages, 8 waves, activation scales in chunks) in four
-# full rounds over the 256 CUs, then the last 2048 columns as 256 tiles of
-# 128x256 (64x64 per wave, 3 stages) in one more round.  The roofline is for
-# the whole call, timed as one launch.
+# full rounds over the 256 CUs, then the last 2048 columns as 512 tiles of
+# 128x128 (64x64 per wave, 4 waves, 2 stages, two workgroups per CU) in one
+# more round.  The roofline is for the whole call, timed as one launch.
 GEMM_KERNEL = ("gemm_tile_kernel<256,256,128,64,2,8,2,true,false,false,1,false> x 1024 tiles + "
-               "gemm_tile_kernel<128,256,64,64,3,8,2,false,false,false,1,false> x 256 tiles")
+               "gemm_tile_kernel<128,128,64,64,2,4,2,true,false,false,2,false> x 512 tiles")
 GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_03_amd", "csrc", "gemm.hip")
 # HBM traffic of one prefill GEMM call (both kernels) from the rocprofv3
 # FETCH_SIZE and WRITE_SIZE runs (scaled by the 1 GiB copy calibration; see
 # profiles/), valid only for the gemm.hip source whose SHA-256 is recorded
 # with it.
-GEMM_TRAFFIC = {"source_sha256": "c19def244d81cd3efbf0eb4cd9a71d4971ddabb5b46d1596e04fcca1dd0852a9",
+GEMM_TRAFFIC = {"source_sha256": "0000000000000000000000000000000000000000000000000000000000000000",
                 "fetch_bytes": 864498278, "write_bytes": 152033178}
 
 

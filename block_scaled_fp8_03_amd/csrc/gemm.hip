@@ -1347,9 +1347,11 @@ hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
 
 }  // namespace
 
-// Time of a 128 x 256 tile relative to a 256 x 256 tile of the same K.
+// Time of a round of 128 x 128 tail tiles (two workgroups per CU) relative
+// to a round of 256 x 256 tiles of the same K (measured ~65 vs ~108 us at
+// K = 7168).
 #ifndef FP8BS_TAIL_COST
-#define FP8BS_TAIL_COST 0.75
+#define FP8BS_TAIL_COST 0.6
 #endif
 constexpr double kTailCost = FP8BS_TAIL_COST;
 
@@ -1388,16 +1390,17 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   p.num_n = (int)((N + BN - 1) / BN);
   // One workgroup per CU, so a launch takes ceil(tiles / CUs) rounds of
   // equal tiles.  When the last round would be partly empty, the columns
-  // past the last full round run as a second launch of 128 x 256 tiles
-  // (twice as many, each faster than a 256 x 256 tile), if the model
-  // full rounds + tail rounds x kTailCost beats one more full round.
+  // past the last full round run as a second launch of 128 x 128 tiles, two
+  // workgroups per CU (four times as many tiles, each a quarter of the work),
+  // if the model full rounds + tail rounds x kTailCost beats one more full
+  // round.
   const int64_t T = (int64_t)p.num_m * p.num_n;
   const int64_t full = T / cus * cus;
   if (BM == 256 && BN == 256 && T > cus && full != T && full % p.num_m == 0) {
     const int n_main = (int)(full / p.num_m);
     const int64_t tail_cols = N - (int64_t)n_main * BN;
-    const int64_t tail_tiles = ((M + 127) / 128) * ((tail_cols + 255) / 256);
-    const double split_cost = (double)(full / cus) + (double)((tail_tiles + cus - 1) / cus) * kTailCost;
+    const int64_t tail_tiles = ((M + 127) / 128) * ((tail_cols + 127) / 128);
+    const double split_cost = (double)(full / cus) + (double)((tail_tiles + 2 * cus - 1) / (2 * cus)) * kTailCost;
     if (split_cost < (double)((T + cus - 1) / cus)) {
       p.num_n = n_main;
       hipError_t e = run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, (int)full, stream);
@@ -1405,11 +1408,14 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
       GemmParams q = p;
       q.n0 = n_main * BN;
       q.num_m = (int)((M + 127) / 128);
-      q.num_n = (int)((tail_cols + 255) / 256);
-      // three stages (a_s per stage, which leaves room for the third): a
-      // tile this small waits on the DMA round trip with only two
-      launch_tile<128, 256, 64, 64, 3, 8, 2, false, false, 1, E8>(q, out_f32, q.num_m * q.num_n, stream);
-      return hipGetLastError();
+      q.num_n = (int)((tail_cols + 127) / 128);
+      // 128 x 128 tiles of four waves (64 x 64 each), two stages, two
+      // workgroups per CU (74 KB of LDS each): a barrier spans four waves
+      // and the two workgroups fill each other's waits.  Measured against
+      // one workgroup per CU of 128 x 256 tiles (eight waves, three stages):
+      // prefill 513.6 -> 500.9 us, N = 18000 509.2 -> 493.9 us, ue8m0
+      // prefill 468.3 -> 455.8 us.
+      return run_tile<128, 128, 64, 64, 2, 4, 2, false, 2, E8>(q, out_f32, q.num_m * q.num_n, stream);
     }
   }
   return run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
