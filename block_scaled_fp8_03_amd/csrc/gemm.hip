@@ -1163,7 +1163,7 @@ w8a16_tile_kernel(GemmParams p) {
     const int gsz = min(p.num_m - first_m, GM);
     const int in = t % group;
     m_base = (first_m + in % gsz) * BM;
-    n_base = (in / gsz) * BN;
+    n_base = p.n0 + (in / gsz) * BN;
   }
 
   const v4i a_rsrc = make_rsrc(p.a, (uint32_t)((int64_t)p.rows * K * 2));
@@ -1535,16 +1535,22 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   return err;
 }
 
+// The grid of p.num_m x p.num_n tiles (columns from p.n0 on).
 template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC>
-hipError_t run_w8a16(GemmParams p, bool out_f32, hipStream_t stream) {
-  p.num_m = (int)((p.rows + BM - 1) / BM);
-  p.num_n = (int)((p.N + BN - 1) / BN);
+hipError_t run_w8a16_grid(const GemmParams& p, bool out_f32, hipStream_t stream) {
   const dim3 grid((unsigned)(p.num_m * p.num_n)), block(NW * 64);
   if (out_f32)
     w8a16_tile_kernel<BM, BN, WM, WN, NW, ST, OCC, true><<<grid, block, 0, stream>>>(p);
   else
     w8a16_tile_kernel<BM, BN, WM, WN, NW, ST, OCC, false><<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int NW, int ST, int OCC>
+hipError_t run_w8a16(GemmParams p, bool out_f32, hipStream_t stream) {
+  p.num_m = (int)((p.rows + BM - 1) / BM);
+  p.num_n = (int)((p.N + BN - 1) / BN);
+  return run_w8a16_grid<BM, BN, WM, WN, NW, ST, OCC>(p, out_f32, stream);
 }
 
 // Tile choice: decode-sized M streams the weight through 64-column tiles
@@ -1571,9 +1577,33 @@ hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, voi
     return hipGetLastError();
   }
   if (M <= 64) return run_w8a16<64, 64, 64, 16, 4, 6, 2>(p, out_f32, stream);
+  const int cus = device_cus();
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles < device_cus()) return run_w8a16<128, 128, 64, 64, 4, 4, 1>(p, out_f32, stream);
-  return run_w8a16<256, 256, 128, 64, 8, 3, 1>(p, out_f32, stream);
+  if (big_tiles < cus) return run_w8a16<128, 128, 64, 64, 4, 4, 1>(p, out_f32, stream);
+  // As in the FP8 GEMM: when the last round of 256 x 256 tiles would be
+  // partly empty, the columns past the last full round run as a second launch
+  // of 128 x 128 tiles (four waves, three stages) two workgroups per CU, if
+  // full rounds + tail rounds x kTailCost beats one more full round.
+  p.num_m = (int)((M + 255) / 256);
+  p.num_n = (int)((N + 255) / 256);
+  const int64_t full = big_tiles / cus * cus;
+  if (full != big_tiles && full % p.num_m == 0) {
+    const int n_main = (int)(full / p.num_m);
+    const int64_t tail_cols = N - (int64_t)n_main * 256;
+    const int64_t tail_tiles = ((M + 127) / 128) * ((tail_cols + 127) / 128);
+    const double split_cost = (double)(full / cus) + (double)((tail_tiles + 2 * cus - 1) / (2 * cus)) * kTailCost;
+    if (split_cost < (double)((big_tiles + cus - 1) / cus)) {
+      p.num_n = n_main;
+      hipError_t e = run_w8a16_grid<256, 256, 128, 64, 8, 3, 1>(p, out_f32, stream);
+      if (e != hipSuccess) return e;
+      GemmParams q = p;
+      q.n0 = n_main * 256;
+      q.num_m = (int)((M + 127) / 128);
+      q.num_n = (int)((tail_cols + 127) / 128);
+      return run_w8a16_grid<128, 128, 64, 64, 4, 3, 2>(q, out_f32, stream);
+    }
+  }
+  return run_w8a16_grid<256, 256, 128, 64, 8, 3, 1>(p, out_f32, stream);
 }
 
 }  // namespace fp8bs

@@ -75,6 +75,7 @@ def test_w8a16_wide_scales():
     (3, 4096, 18432, 7168),      # prefill up-projection shape
     (3, 4096, 7168, 18432),      # prefill down-projection shape
     (2, 32, 18432, 7168),        # decode shape
+    (3, 4000, 18000, 1024),      # ragged M and N, with the launch split into 256x256 and 128x128 tiles
 ])
 def test_w8a16_full_size_sampled(cfg, M, N, K):
     """Full-size shapes (inputs drawn on the host and quantised by the oracle),
@@ -85,7 +86,8 @@ def test_w8a16_full_size_sampled(cfg, M, N, K):
     torch.cuda.synchronize()
     rng = np.random.default_rng(cfg * 100 + N)
     rows = [0, M - 1, min(255, M - 1), min(256, M - 1)] + list(rng.integers(0, M, 2))
-    cols = [0, N - 1, 255, 256] + list(rng.integers(0, N, 2))
+    # 16383 / 16384: the last column of the 256x256 launch and the first of the 128x128 one
+    cols = [0, N - 1, 255, 256] + [c for c in (16383, 16384) if c < N] + list(rng.integers(0, N, 2))
     pr = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 2000)])
     pc = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 2000)])
     xb = inputs.bf16_bits(x)
