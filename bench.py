@@ -58,7 +58,7 @@ GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_03_amd", "csrc", "gemm.hip")
 # FETCH_SIZE and WRITE_SIZE runs (scaled by the 1 GiB copy calibration; see
 # profiles/), valid only for the gemm.hip source whose SHA-256 is recorded
 # with it.
-GEMM_TRAFFIC = {"source_sha256": "6827d27344e434f01d2cb144dc6d5a108124b93d622dbc6e5789ff165c2656f0",
+GEMM_TRAFFIC = {"source_sha256": "e0048e3322e7d631e35acc74c8ec35c66cd12f5cb3ea6dfc95ae47eec9353340",
                 "fetch_bytes": 869522842, "write_bytes": 152078950}
 
 
