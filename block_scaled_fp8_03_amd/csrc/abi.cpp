@@ -101,7 +101,7 @@ int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64
                          void* stream) {
   if (N < 0 || K < 0) return FP8BS_ERR_SHAPE;
   const int64_t n = mul(N, K);
-  if (n < 0 || mul(n, 2) < 0 || cdiv(N, 16) > 65535) return FP8BS_ERR_SHAPE;
+  if (n < 0 || mul(n, 2) < 0 || !fp8bs::weight_dequant_fits(N, K)) return FP8BS_ERR_SHAPE;
   if (n == 0) return FP8BS_OK;
   if (!w_e4m3 || !s || !y_bf16) return FP8BS_ERR_NULL;
   if (!aligned(w_e4m3, 16) || !aligned(y_bf16, 16) || !aligned(s, 4)) return FP8BS_ERR_ALIGN;

@@ -12,6 +12,8 @@ hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t
                             hipStream_t stream);
 hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K, bool ue8m0,
                                hipStream_t stream);
+// Whether one weight_dequant launch covers [N, K] (its grid's thread limit).
+bool weight_dequant_fits(int64_t N, int64_t K);
 hipError_t launch_weight_dequant(const void* w, const float* s, void* y, int64_t N, int64_t K,
                                  hipStream_t stream);
 hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kScanThreads) void moe_route_scan_kernel(int32_t* _
         for (int j = 0; j < kBatch; ++j)
           if (c0 + j < C) hist[(int64_t)(c0 + j) * E + e] = v[j];
       }
-    // exclusive prefix of the totals over the experts of this round
+    // exclusive prefix of the totals over the experts of this pass
     part[threadIdx.x] = tot;
     __syncthreads();
     for (int d = 1; d < kScanThreads; d <<= 1) {

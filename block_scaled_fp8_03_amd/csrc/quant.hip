@@ -235,53 +235,44 @@ hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int6
 // ----------------------------------------------------------------------------
 // weight_dequant
 // ----------------------------------------------------------------------------
-// Vector path (K % 16 == 0): lane l of wave w handles the 16-column chunk
-// blockIdx.x*64 + l of rows blockIdx.y*kDqRows + w + 4i; a chunk never
-// straddles a 128-column scale block.  Per row: one 16-byte load, 16
-// conversions, 16 multiplies, 8 bf16 pair packs, one 32-byte store.  Four
-// rows per workgroup (one per wave) measured fastest: 18432 x 7168 with
-// inputs from HBM 82.5 / 76.1 / 71.0 us at 16 / 8 / 4 rows, 86.6 at 32; a
-// non-temporal load added nothing at 4 rows, non-temporal stores cost 27%.
+// Vector path (K % 16 == 0): a one-dimensional grid of ceil(N / kDqRows) x
+// ceil(K / 1024) workgroups, the column span fastest (bx = span, by = row
+// group).  Wave w converts row by*kDqRows + w over 1024 columns; lane l takes
+// the 8-column chunks bx*128 + l and bx*128 + l + 64 (8 e4m3 bytes in, 16 bf16 bytes out; a
+// chunk never straddles a 128-column scale block).  Each of a wave's two
+// 16-byte stores then writes 1 KB of contiguous output, whole cache lines;
+// the earlier mapping (one 16-byte load and two 16-byte stores per lane for
+// 16 consecutive columns) left every store instruction writing half of each
+// line it touched.  The stores carry the non-temporal hint.  N x 7168 with
+// two weights in rotation, same box, us (before / remap / remap + hint):
+// N = 4096 15.4 / 14.1 / 13.9, 9216 38.8 / 35.8 / 29.7, 16384 63.3 / 60.1 /
+// 52.5, 18432 70.8 / 67.7 / 59.2, 36864 137.7 / 133.0 / 129.3; non-temporal
+// loads as well cost (18432: 62.3).  Four rows per workgroup (one per wave)
+// measured fastest in the earlier mapping: 82.5 / 76.1 / 71.0 us at 16 / 8 /
+// 4 rows, 86.6 at 32.
 constexpr int kDqRows = 4;
 
-__global__ __launch_bounds__(256) void weight_dequant_kernel(const uint4* __restrict__ w,
-                                                             const float* __restrict__ s,
-                                                             uint4* __restrict__ y, int64_t N,
-                                                             int64_t K) {
+__global__ __launch_bounds__(64 * kDqRows) void weight_dequant_kernel(const uint2* __restrict__ w,
+                                                                      const float* __restrict__ s,
+                                                                      uint4* __restrict__ y,
+                                                                      int64_t N, int64_t K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t kc = (int64_t)blockIdx.x * 64 + lane;      // 16-element chunk in the row
-  const int64_t kchunks = K / 16;
-  if (kc >= kchunks) return;
+  const int64_t kc8 = K / 8;                                 // 8-column chunks per row
+  const int64_t spans = (kc8 + 127) / 128;
+  const int64_t c0 = ((int64_t)blockIdx.x % spans) * 128 + lane;
+  const int64_t n = ((int64_t)blockIdx.x / spans) * kDqRows + wave;
+  if (c0 >= kc8 || n >= N) return;
+  const bool has1 = c0 + 64 < kc8;
   const int64_t nbk = (K + kBlock - 1) / kBlock;
-  const int64_t sb = (kc * 16) / kBlock;
-  constexpr int kPer = kDqRows / 4;
-  uint4 v[kPer];
-  float sc[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t n = (int64_t)blockIdx.y * kDqRows + wave + 4 * i;
-    if (n < N) {
-      v[i] = w[n * kchunks + kc];
-      sc[i] = s[(n / kBlock) * nbk + sb];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t n = (int64_t)blockIdx.y * kDqRows + wave + 4 * i;
-    if (n >= N) continue;
-    const uint32_t ws[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    uint32_t o[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);   // bytes 0, 1
-      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);    // bytes 2, 3
-      o[2 * j] = pack2_bf16(__fmul_rn(lo.x, sc[i]), __fmul_rn(lo.y, sc[i]));
-      o[2 * j + 1] = pack2_bf16(__fmul_rn(hi.x, sc[i]), __fmul_rn(hi.y, sc[i]));
-    }
-    uint4* dst = y + (n * kchunks + kc) * 2;
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  }
+  const float* srow = s + (n / kBlock) * nbk;
+  const uint2 v0 = w[n * kc8 + c0];
+  const uint2 v1 = has1 ? w[n * kc8 + c0 + 64] : make_uint2(0, 0);
+  const float s0 = srow[(c0 * 8) / kBlock];
+  const float s1 = has1 ? srow[((c0 + 64) * 8) / kBlock] : 0.0f;
+  const uint4 o0 = __builtin_bit_cast(uint4, dequant8_bf16(v0.x, v0.y, s0));
+  const uint4 o1 = __builtin_bit_cast(uint4, dequant8_bf16(v1.x, v1.y, s1));
+  store_nt(y + n * kc8 + c0, o0);
+  if (has1) store_nt(y + n * kc8 + c0 + 64, o1);
 }
 
 // Generic path (any K): one element per thread.
@@ -298,13 +289,25 @@ __global__ __launch_bounds__(256) void weight_dequant_scalar_kernel(const uint8_
   y[i] = (uint16_t)(pack2_bf16(p, 0.0f) & 0xFFFFu);
 }
 
+// Both grids are one-dimensional: at most 2^32 - 1 threads.
+bool weight_dequant_fits(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return true;
+  const int64_t limit = ((int64_t)1 << 32) - 1;
+  if (K % 16 == 0) {
+    const int64_t spans = (K / 8 + 127) / 128, groups = (N + kDqRows - 1) / kDqRows;
+    return groups <= limit / (64 * kDqRows) / spans;
+  }
+  return N <= (limit - 255) / K;
+}
+
 hipError_t launch_weight_dequant(const void* w, const float* s, void* y, int64_t N, int64_t K,
                                  hipStream_t stream) {
   if (N == 0 || K == 0) return hipSuccess;
+  if (!weight_dequant_fits(N, K)) return hipErrorInvalidConfiguration;
   if (K % 16 == 0) {
-    const int64_t gx = (K / 16 + 63) / 64, gy = (N + kDqRows - 1) / kDqRows;
-    weight_dequant_kernel<<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream>>>(
-        (const uint4*)w, s, (uint4*)y, N, K);
+    const int64_t spans = (K / 8 + 127) / 128, groups = (N + kDqRows - 1) / kDqRows;
+    const dim3 grid((unsigned)(spans * groups)), block(64 * kDqRows);
+    weight_dequant_kernel<<<grid, block, 0, stream>>>((const uint2*)w, s, (uint4*)y, N, K);
   } else {
     const int64_t grid = (N * K + 255) / 256;
     weight_dequant_scalar_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(

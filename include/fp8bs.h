@@ -105,7 +105,10 @@ int fp8bs_weight_quant(const void* w_bf16, void* q_e4m3, float* s, int64_t N, in
  *   w_e4m3  in   e4m3 [N, K]
  *   s       in   float32 [ceil(N/128), ceil(K/128)]
  *   y_bf16  out  bf16 [N, K]
- *   N, K >= 0, any values (ragged edge blocks allowed).
+ *   N, K >= 0, ragged edge blocks allowed.  One launch covers at most 2^32 - 1
+ *   threads: N*K + 255 < 2^32 when K % 16 != 0, and ceil(N/4) * ceil(K/1024)
+ *   < 2^24 workgroups when K % 16 == 0 (N*K up to about 2^36); larger shapes
+ *   return FP8BS_ERR_SHAPE.
  */
 int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64_t N, int64_t K,
                          void* stream);

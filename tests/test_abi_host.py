@@ -83,6 +83,23 @@ def test_weight_quant_and_dequant_validation(L):
     assert L.fp8bs_weight_dequant(None, None, None, 7, 0, None) == OK
 
 
+def test_weight_dequant_launch_limits(L):
+    """One launch covers at most 2^32 - 1 threads: N*K + 255 < 2^32 for
+    K % 16 != 0, ceil(N/4) * ceil(K/1024) < 2^24 workgroups for K % 16 == 0.
+    Shapes just inside pass the shape check and stop at the null pointers."""
+    d = L.fp8bs_weight_dequant
+    assert d(P0, P1, P2, 1 << 20, 4097, None) == SHAPE           # 4296015872 elements
+    assert d(None, None, None, 1 << 20, 4095, None) == NULL      # 4293918720 + 255 < 2^32
+    assert d(None, None, None, (2 ** 32 - 256) // 3, 3, None) == NULL
+    assert d(P0, P1, P2, (2 ** 32 - 256) // 3 + 1, 3, None) == SHAPE
+    assert d(P0, P1, P2, 1 << 26, 1024, None) == SHAPE           # 2^24 workgroups
+    assert d(None, None, None, (1 << 26) - 4, 1024, None) == NULL  # 2^24 - 1
+    assert d(P0, P1, P2, (1 << 26) - 3, 1024, None) == SHAPE     # ceil(N/4) = 2^24
+    assert d(None, None, None, 1048592, 128, None) == NULL       # more than 2^20 rows
+    assert d(None, None, None, (1 << 25) - 8, 1040, None) == NULL  # (2^23 - 2) x 2 spans
+    assert d(P0, P1, P2, 1 << 25, 1040, None) == SHAPE           # 2^23 groups x 2 spans
+
+
 @pytest.mark.parametrize("name", ["fp8bs_gemm", "fp8bs_gemm_ue8m0"])
 def test_gemm_validation(L, name):
     g = getattr(L, name)

@@ -140,3 +140,44 @@ def test_mla_prefill_sampled():
         got = out[torch.from_numpy(ts).to(DEV), torch.from_numpy(hs).to(DEV),
                   torch.from_numpy(cs).to(DEV)].cpu().numpy().astype(np.float64)
         check(got, ref, S, False, f"mla prefill sampled side {side}")
+
+
+@pytest.mark.parametrize("T,H,dn,R", [(100, 2, 128, 640), (200, 1, 256, 896), (70, 3, 128, 1152)])
+def test_mla_key_partial_workgroup(T, H, dn, R):
+    """Key side with R not a multiple of 512: the last workgroup of eight
+    waves has idle waves, and its staged bf16 rows stop at R."""
+    dv = 128
+    q, s = wkv_b(H, dn, dv, R, 650 + T + R)
+    x = inputs.normal_bf16((T, H, dn), 1.0, 660 + T)
+    xb = inputs.bf16_bits(x)
+    ref = oracle.mla_absorb(KEY, xb, q, s, dn, dv)
+    S = oracle.mla_absorb(KEY, xb & 0x7FFF, q & 0x7F, np.abs(s), dn, dv)
+    xd = x.to(DEV)
+    check(run(KEY, xd, q, s, dn, dv, torch.float32), ref, S, False, f"mla key [{T},{H},{dn},{R}] f32")
+    check(run(KEY, xd, q, s, dn, dv, torch.bfloat16), ref, S, True, f"mla key [{T},{H},{dn},{R}] bf16")
+
+
+@pytest.mark.parametrize("T", [4096, 2048, 1000])
+def test_mla_prefill_bf16_is_rounded_f32(T):
+    """Both output types come from the same float32 accumulators, so every
+    bf16 output must be the float32 output rounded to nearest even, bit for
+    bit, over the whole tensor.  At 128 heads this covers the launches whose
+    large stream (key output, value input) takes the non-temporal hint (4096
+    and 2048 tokens) and those below the cut (1000 tokens), including the
+    staged rows of the ragged last token tile; the float32 output itself is
+    checked against the oracle at 4096 tokens by test_mla_prefill_sampled."""
+    m = inputs.MLA
+    H, dn, dv, R = m["heads"], m["dn"], m["dv"], m["R"]
+    q, s = wkv_b(H, dn, dv, R, inputs.seed_for(inputs.MLA["seed_id"], 1))
+    qd, sd = to_dev_u8(q), to_dev_f32(s)
+    for side, width in ((KEY, dn), (VALUE, R)):
+        fn = fp8bs.mla_absorb_key if side == KEY else fp8bs.mla_absorb_value
+        x = inputs.normal_bf16_device((T, H, width), 1.0, 670 + side, DEV)
+        o32 = fn(x, qd, sd, dn, dv, torch.float32)
+        o16 = fn(x, qd, sd, dn, dv, torch.bfloat16)
+        torch.cuda.synchronize()
+        want = o32.to(torch.bfloat16)
+        same = o16.view(torch.int16) == want.view(torch.int16)
+        assert bool(same.all()), (f"side {side} T={T}: {int((~same).sum())} bf16 outputs differ, "
+                                  f"first {torch.nonzero(~same)[:4].tolist()}")
+        del x, o32, o16, want, same

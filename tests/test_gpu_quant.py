@@ -119,10 +119,15 @@ def check_dequant(q: np.ndarray, s: np.ndarray, what: str):
     assert_bytes_equal(np.where(nan_ref, 0, got), np.where(nan_ref, 0, ref), what)
 
 
-@pytest.mark.parametrize("N,K", [(256, 256), (257, 200), (130, 384), (131, 1040), (1, 16), (3, 5)])
+@pytest.mark.parametrize("N,K", [(256, 256), (257, 200), (130, 384), (131, 1040), (1, 16), (3, 5),
+                                 (5, 1824), (9103, 14880)])
 def test_weight_dequant_all_codes(N, K):
     """Every code (NaN included) against a spread of scales, ragged edges, both
-    the 16-wide vector path (K % 16 == 0) and the element path."""
+    the vector path (K % 16 == 0) and the element path.  In the vector path a
+    lane takes 8-column chunks c and c + 64 of a 1024-column span: K = 1040
+    and 1824 leave a last span where only some lanes (or none) have the second
+    chunk, and N not a multiple of 4 leaves idle waves in the last row group;
+    9103 x 14880 has 15 spans."""
     rng = np.random.default_rng(N * 31 + K)
     q = rng.integers(0, 256, (N, K), dtype=np.uint8)
     q.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)[: q.size]
