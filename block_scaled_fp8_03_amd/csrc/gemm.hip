@@ -198,6 +198,54 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
 // (v_mfma_scale_f32_16x16x128_f8f6f4 with each lane's E8M0 exponent: the
 // weight block's for the weight operand, its activation row's for the other)
 // and accumulates straight into the fp32 accumulators -- no VALU fold.
+// bf16 C tile out through LDS.  Lane (r16, g) of wave (wm, wn) holds
+// C[row][col .. col+3] for row = wm*WM + 16t + r16, col = wn*WN + 16j + 4g;
+// written straight to global memory, each store instruction would cover 32
+// bytes of each of 16 rows, a quarter of every line it touches.  Instead the
+// tile goes into the (drained) stage buffers as BM rows of BN bf16, 16-byte
+// chunk c of row r at c ^ (r mod 16) (conflict-free for both the 8-byte
+// writes and the 16-byte reads), then every thread writes whole 16-byte
+// chunks of consecutive columns, a wave covering whole rows, with the
+// non-temporal hint.  Rows from m_end and columns from N are not stored
+// (N % 8 == 0, so a chunk is all in or all out).  Same box, bit-identical
+// outputs (us, before -> after): 4096x18432x7168 500 -> 491, 1024x16384x512
+// 18.6 -> 15.7, MoE up / down 1050 / 1157 -> 1016 / 1114; the down GEMM
+// 4096x7168x18432 unchanged (485.5 -> 485.1).  The caller guarantees that no
+// wave still reads the stage buffers' operands (the barrier below) and that
+// no DMA into them is in flight.
+template <int BM, int BN, int WM, int WN, int NW, int MT, int NT>
+__device__ __forceinline__ void store_c_tile_bf16(uint8_t* smem, const v4f (&acc)[NT][MT], int tid,
+                                                  int wm, int wn, void* c_out, int N, int m_base,
+                                                  int m_end, int n_base) {
+  constexpr int CPRC = BN / 8;                                // 16-byte chunks per C row
+  constexpr int SWM = CPRC >= 16 ? 15 : CPRC - 1;
+  constexpr int PASSES = BM * CPRC / (NW * 64);
+  static_assert((CPRC & (CPRC - 1)) == 0, "power-of-two row chunks");
+  static_assert(BM * CPRC % (NW * 64) == 0, "whole passes");
+  const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int row = wm * WM + 16 * t + r16;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = (wn * WN + 16 * j) / 8 + (g >> 1);
+      const uint32_t lo = pack2_bf16(acc[j][t][0], acc[j][t][1]);
+      const uint32_t hi = pack2_bf16(acc[j][t][2], acc[j][t][3]);
+      *(uint2*)(smem + row * (BN * 2) + ((c ^ (row & SWM)) << 4) + 8 * (g & 1)) = make_uint2(lo, hi);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int q = tid + ps * NW * 64;
+    const int row = q / CPRC, c = q % CPRC;
+    const int m = m_base + row, n = n_base + 8 * c;
+    const uint4 v = *(const uint4*)(smem + row * (BN * 2) + ((c ^ (row & SWM)) << 4));
+    if (m < m_end && n < N) store_nt((uint4*)((uint16_t*)c_out + (int64_t)m * N + n), v);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool MOE,
           int OCC, bool E8 = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))
@@ -463,6 +511,14 @@ gemm_tile_kernel(GemmParams p) {
   }
 
   // ---- epilogue: lane holds C[m][n .. n+3] for each (j, t)
+  if constexpr (!OUT_F32) {
+    if ((N & 7) == 0) {
+      static_assert(BM * BN * 2 <= ST * STAGE, "the C tile fits the stage buffers");
+      store_c_tile_bf16<BM, BN, WM, WN, NW, MT, NT>(smem, acc, tid, wm, wn, p.c, N, m_base, m_end,
+                                                    n_base);
+      return;
+    }
+  }
   const bool vec_ok = (N % 4) == 0;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -1243,6 +1299,14 @@ w8a16_tile_kernel(GemmParams p) {
   }
 
   // ---- epilogue: lane holds C[m][n .. n+3] for each (j, t)
+  if constexpr (!OUT_F32) {
+    if ((N & 7) == 0) {
+      static_assert(BM * BN * 2 <= ST * STAGE, "the C tile fits the stage buffers");
+      store_c_tile_bf16<BM, BN, WM, WN, NW, MT, NT>(smem, acc, tid, wm, wn, p.c, N, m_base, p.rows,
+                                                    n_base);
+      return;
+    }
+  }
   const bool vec_ok = (N % 4) == 0;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
