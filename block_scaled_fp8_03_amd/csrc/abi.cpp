@@ -59,7 +59,7 @@ int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64
   if (M < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (scale_fmt != FP8BS_SCALE_FP32 && scale_fmt != FP8BS_SCALE_UE8M0) return FP8BS_ERR_ENUM;
   const int64_t n = mul(M, K);
-  if (n < 0 || mul(n, 2) < 0) return FP8BS_ERR_SHAPE;
+  if (n < 0 || mul(n, 2) < 0 || !fp8bs::act_quant_fits(M, K)) return FP8BS_ERR_SHAPE;
   if (n == 0) return FP8BS_OK;
   if (!x_bf16 || !q_e4m3 || !s) return FP8BS_ERR_NULL;
   if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(s, 4)) return FP8BS_ERR_ALIGN;
@@ -275,7 +275,8 @@ int fp8bs_moe_quant_scatter(const void* x_bf16, const int32_t* row_of, void* q_e
   if (T < 0 || topk < 1 || R < 0 || K < 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (scale_fmt != FP8BS_SCALE_FP32 && scale_fmt != FP8BS_SCALE_UE8M0) return FP8BS_ERR_ENUM;
   const int64_t nx = mul(T, K), nq = mul(R, K), P = mul(T, topk);
-  if (nx < 0 || nq < 0 || P < 0 || P > kLimitInt || mul(nx, 2) < 0 || R > kLimitInt)
+  if (nx < 0 || nq < 0 || P < 0 || P > kLimitInt || mul(nx, 2) < 0 || R > kLimitInt ||
+      !fp8bs::act_quant_fits(T, K))
     return FP8BS_ERR_SHAPE;
   if (nx == 0 || nq == 0) return FP8BS_OK;
   if (!x_bf16 || !row_of || !q_e4m3 || !s) return FP8BS_ERR_NULL;

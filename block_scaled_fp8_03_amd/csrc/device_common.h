@@ -20,14 +20,17 @@ __device__ __forceinline__ float bits_f32(uint32_t u) { return __uint_as_float(u
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
 
 // Streaming (read-once / write-once) memory accesses: the non-temporal hint
-// keeps data that is not reused from displacing what is.  Measured (same-box
-// A/B, inputs larger than the caches): act_quant 4096 x 18432 42.3 -> 39.5 us,
-// MoE quant_scatter 67.9 -> 62.0 us, MoE combine 101.9 -> 89.2 us; on
-// weight_dequant it cost 2% and is not used there.  The stores pay only where
-// a wave writes whole cache lines: on the GEMM and MLA epilogues, whose lanes
-// write 8-16 bytes at a row stride, they were several times slower.
-// kNonTemporal is the cache-policy operand of the raw buffer load builtins
-// (the `nt` bit on gfx950).
+// keeps data that is not reused from displacing what is.  It pays where a
+// store instruction writes whole cache lines (a wave's lanes covering
+// contiguous bytes) or a load streams data read once: act_quant's input and
+// codes, the MoE quant_scatter and combine, weight_dequant's output (after
+// its lanes were remapped so each store writes 1 KB contiguous), the GEMM's
+// bf16 C tile written as whole rows from LDS, the MLA key output staged the
+// same way, and the weight DMA of the decode and small-expert MoE tiles.
+// Where lanes write 8-16 bytes at a row stride (a store covering part of
+// every line it touches) the hint made the stores several times slower, so
+// such stores stay plain.  kNonTemporal is the cache-policy operand of the
+// raw buffer load builtins (the `nt` bit on gfx950).
 constexpr int kNonTemporal = 2;
 template <typename T>
 __device__ __forceinline__ void store_nt(T* p, const T& v);

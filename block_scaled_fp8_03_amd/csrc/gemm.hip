@@ -1414,10 +1414,7 @@ hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
 // Time of a round of 128 x 128 tail tiles (two workgroups per CU) relative
 // to a round of 256 x 256 tiles of the same K (measured ~65 vs ~108 us at
 // K = 7168).
-#ifndef FP8BS_TAIL_COST
-#define FP8BS_TAIL_COST 0.6
-#endif
-constexpr double kTailCost = FP8BS_TAIL_COST;
+constexpr double kTailCost = 0.6;
 
 template <bool E8>
 hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
@@ -1429,11 +1426,9 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   if (M <= 16) return run_decode<1>(p, out_f32, stream);
   if (M <= 32) return run_decode<2>(p, out_f32, stream);
   if (M <= 64) return run_decode<4>(p, out_f32, stream);
-#ifndef FP8BS_TILE_CFG
-#define FP8BS_TILE_CFG 256, 256, 128, 64, 2, 8, 2
-#endif
-  constexpr int cfg[7] = {FP8BS_TILE_CFG};
-  constexpr int BM = cfg[0], BN = cfg[1];
+  // The main tile: 256 x 256, eight waves of 128 (m) x 64 (n), two LDS
+  // stages, the conflict-free swizzle.
+  constexpr int BM = 256, BN = 256;
   // Smaller GEMMs whose 256 x 256 tiles cannot fill the CUs run on 128 x 128
   // tiles when those give at least one tile per two CUs, else on 64 x 64
   // tiles with two workgroups per CU (measured: 1024 x 1536 x 7168 104 ->
@@ -1467,7 +1462,7 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
     const double split_cost = (double)(full / cus) + (double)((tail_tiles + 2 * cus - 1) / (2 * cus)) * kTailCost;
     if (split_cost < (double)((T + cus - 1) / cus)) {
       p.num_n = n_main;
-      hipError_t e = run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, (int)full, stream);
+      hipError_t e = run_tile<256, 256, 128, 64, 2, 8, 2, false, 1, E8>(p, out_f32, (int)full, stream);
       if (e != hipSuccess) return e;
       GemmParams q = p;
       q.n0 = n_main * BN;
@@ -1482,7 +1477,7 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
       return run_tile<128, 128, 64, 64, 2, 4, 2, false, 2, E8>(q, out_f32, q.num_m * q.num_n, stream);
     }
   }
-  return run_tile<FP8BS_TILE_CFG, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<256, 256, 128, 64, 2, 8, 2, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
 }
 
 hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
@@ -1548,10 +1543,7 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   // 64-row tiles with three LDS stages.  Each launch finds its experts from
   // the device offsets; the grids are upper bounds on its tile count
   // (tiles past the end exit at once).
-#ifndef FP8BS_MOE_SPLIT
-#define FP8BS_MOE_SPLIT 64
-#endif
-  constexpr int kMoeSplit = FP8BS_MOE_SPLIT;
+  constexpr int kMoeSplit = 64;
   // The two classes run side by side (the small experts on the side stream):
   // under skewed routing one is bound by the matrix cores and the other by
   // HBM, and each grid's last round of workgroups is only partly full, so

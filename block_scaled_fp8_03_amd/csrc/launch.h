@@ -8,6 +8,9 @@
 
 namespace fp8bs {
 
+// Whether one act_quant (or moe_quant_scatter) launch covers `rows` rows of
+// K columns (its grid's thread limit).
+bool act_quant_fits(int64_t rows, int64_t K);
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
                             hipStream_t stream);
 hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K, bool ue8m0,

@@ -25,14 +25,8 @@ namespace fp8bs {
 // 512 x 2, 1024 x 2, 512 x 4, 256 x 4 and 512 x 1 on every workload (same box:
 // 4096 x 18432 39.4 -> 38.3 us, 32768 x 2048 35.0 -> 34.1 us, 1024 x 7168 ue8m0
 // 6.5 -> 6.0 us, 4096 x 7168 cache-resident 16.3 -> 15.8 us, against 512 x 2).
-#ifndef FP8BS_AQ_THREADS
-#define FP8BS_AQ_THREADS 256
-#endif
-#ifndef FP8BS_AQ_PASSES
-#define FP8BS_AQ_PASSES 2
-#endif
-constexpr int kAqThreads = FP8BS_AQ_THREADS;
-constexpr int kAqPasses = FP8BS_AQ_PASSES;
+constexpr int kAqThreads = 256;
+constexpr int kAqPasses = 2;
 constexpr int kAqBlocksPerWg = (kAqThreads / 16) * kAqPasses;
 
 // SCATTER: x is the token matrix [T, K] and the codes and scale of token t's
@@ -109,10 +103,20 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
   }
 }
 
+// The grid is one-dimensional, ceil(nblocks / kAqBlocksPerWg) workgroups of
+// kAqThreads threads: at most 2^32 - 1 threads per launch.
+bool act_quant_fits(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0) return true;
+  const int64_t max_wg = (((int64_t)1 << 32) - 1) / kAqThreads;
+  const int64_t nb = K / kBlock;
+  return rows <= max_wg * kAqBlocksPerWg / nb;
+}
+
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
                             hipStream_t stream) {
   const int64_t nblocks = M * (K / kBlock);
   if (nblocks == 0) return hipSuccess;
+  if (!act_quant_fits(M, K)) return hipErrorInvalidConfiguration;
   const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
   if (ue8m0)
     act_quant_kernel<true, false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
@@ -129,6 +133,7 @@ hipError_t launch_moe_quant_scatter(const void* x, const int32_t* row_of, void* 
   const int64_t nb = K / kBlock;
   const int64_t nblocks = T * nb;
   if (nblocks == 0 || R == 0) return hipSuccess;
+  if (!act_quant_fits(T, K)) return hipErrorInvalidConfiguration;
   const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
   if (ue8m0)
     act_quant_kernel<true, true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(

@@ -78,6 +78,9 @@ int fp8bs_version(void);
  *   q_e4m3  out  e4m3 [M, K]          (must not overlap x)
  *   s       out  float32 [M, K/128]
  *   M >= 0 (0 = no-op), K >= 0 with K % 128 == 0 (else FP8BS_ERR_SHAPE).
+ *   One launch covers at most 2^32 - 1 threads, 32 blocks per 256 threads:
+ *   M * (K / 128) <= 536870880 (M * K up to about 2^36); larger shapes
+ *   return FP8BS_ERR_SHAPE.
  *   All three pointers 16-byte aligned except `s` (4-byte).
  */
 int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64_t K,
@@ -128,6 +131,21 @@ int fp8bs_weight_dequant(const void* w_e4m3, const float* s, void* y_bf16, int64
  *   M >= 0 (0 = no-op), N >= 0, K >= 128 with K % 128 == 0;
  *   (M + 256) * K < 2^32 and (N + 256) * K < 2^32 (32-bit operand offsets).
  *   a, b, c 16-byte aligned; a_s, b_s 4-byte aligned.
+ *
+ * Accuracy.  Let S[m, n] = sum_kb sum_{k in kb} |a[m,k] * b[n,k]| * a_s[m,kb]
+ * * b_s[n/128,kb] (the sum of the absolute scaled products) and ref the exact
+ * sum.  M <= 64 runs on bf16 matrix instructions over exactly decoded codes;
+ * its float32 result carries only the float32 rounding of the accumulation,
+ * within about (K/128 + 16) * 2^-24 * S of ref.  M > 64 runs on the FP8 matrix instruction
+ * (K = 128 per instruction), whose internal sum of a block's 128 products is
+ * not exact in float32: measured on gfx950 its error per block reaches about
+ * 1.4e-5 of the block's sum of |products| on normally distributed codes and
+ * 2^-13.6 of it with 1% of activations scaled by 50.  The float32 result
+ * then satisfies |err| <= 1e-2 * |ref| + 1e-3 + 2^-11 * S.  Where products
+ * cancel (|ref| much smaller than S) the first two terms alone can be missed:
+ * with 1% x50 activation outliers about 1 output in 10^4 did (211 of 1.57 M
+ * at 1024 x 1536 x 7168); on N(0,1) activations none were seen.  A bf16
+ * output adds its own rounding, 2^-9 * |ref|.
  */
 int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
                int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
@@ -174,6 +192,9 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
  * PRECONDITION (not checked on the host: the scales live on the device):
  * every a_s and b_s value is 2^k with -126 <= k <= 127; only the exponent
  * field is read, so other values give wrong results, not faults.
+ * Accuracy as fp8bs_gemm: M > 64 uses the same FP8 matrix instruction
+ * (scaled form) and has the same 2^-11 * S term beyond
+ * 1e-2 * |ref| + 1e-3; M <= 64 runs fp8bs_gemm's bf16 decode kernel.
  */
 int fp8bs_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
                      int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
@@ -254,7 +275,8 @@ int fp8bs_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E, 
  *   scale_fmt     FP8BS_SCALE_FP32 or FP8BS_SCALE_UE8M0
  * Alignment as fp8bs_act_quant; row_of 4-byte aligned.  If row_of maps two
  * pairs to one row, that row receives one of the two (identical for a
- * token's own duplicates).
+ * token's own duplicates).  Launch limit as fp8bs_act_quant with M = T:
+ * T * (K / 128) <= 536870880, else FP8BS_ERR_SHAPE.
  */
 int fp8bs_moe_quant_scatter(const void* x_bf16, const int32_t* row_of, void* q_e4m3, float* s,
                             int64_t T, int64_t topk, int64_t R, int64_t K, int scale_fmt,

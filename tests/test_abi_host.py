@@ -83,6 +83,23 @@ def test_weight_quant_and_dequant_validation(L):
     assert L.fp8bs_weight_dequant(None, None, None, 7, 0, None) == OK
 
 
+def test_act_quant_launch_limits(L):
+    """One act_quant launch covers at most 2^32 - 1 threads: 256-thread
+    workgroups of 32 blocks, so M * (K / 128) <= 16777215 * 32 = 536870880
+    blocks.  Shapes just inside pass the shape check and stop at the null
+    pointers; just outside they are rejected as shapes.  moe_quant_scatter
+    has the same limit on its T token rows."""
+    f = L.fp8bs_act_quant
+    lim = ((2 ** 32 - 1) // 256) * 32
+    assert f(None, None, None, lim, 128, 0, None) == NULL
+    assert f(P0, P1, P2, lim + 1, 128, 0, None) == SHAPE
+    assert f(None, None, None, lim // 56, 7168, 1, None) == NULL
+    assert f(P0, P1, P2, lim // 56 + 1, 7168, 1, None) == SHAPE
+    g = L.fp8bs_moe_quant_scatter
+    assert g(None, None, None, None, lim // 2, 8, 64, 256, 0, None) == NULL
+    assert g(P0, P1, P2, P3, lim // 2 + 1, 8, 64, 256, 0, None) == SHAPE
+
+
 def test_weight_dequant_launch_limits(L):
     """One launch covers at most 2^32 - 1 threads: N*K + 255 < 2^32 for
     K % 16 != 0, ceil(N/4) * ceil(K/1024) < 2^24 workgroups for K % 16 == 0.

@@ -438,25 +438,27 @@ def test_routing_invariants():
 
 # ---------------------------------------------------- MoE dispatch and combine
 
-def _where_loop_rows(indices, E):
-    """The pages' expert loop (Admin guide 6.4): for each expert, the (token,
-    slot) pairs routed to it, in the order torch.where yields them."""
-    rows = []
-    for e in range(E):
-        tok, slot = np.nonzero(indices == e)
-        rows += list(zip(tok.tolist(), slot.tolist()))
-    return rows
+def _stable_sort_rows(indices, E):
+    """The row order the pages' expert loop gives (Admin guide 6.4: experts in
+    index order, and within an expert its (token, slot) pairs in row-major
+    order), written as a stable sort of the flattened ids: equal ids keep
+    their (token, slot) order."""
+    flat = indices.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    order = order[(flat[order] >= 0) & (flat[order] < E)]
+    topk = indices.shape[1]
+    return [(int(p) // topk, int(p) % topk) for p in order]
 
 
 @pytest.mark.parametrize("T,topk,E,seed", [(1, 1, 1, 0), (7, 3, 5, 1), (64, 8, 16, 2), (300, 8, 64, 3)])
-def test_moe_route_matches_where_loop(orc, T, topk, E, seed):
-    """The counting sort against the per-expert torch.where formulation (a
-    different algorithm): same rows in the same order, offsets = bincount
+def test_moe_route_matches_stable_sort(orc, T, topk, E, seed):
+    """The counting sort against a library stable sort of the flattened ids
+    (a different algorithm): same rows in the same order, offsets = bincount
     prefix sums, row_of the inverse map.  Ids may repeat within a token."""
     rng = np.random.default_rng(seed)
     idx = rng.integers(0, E, (T, topk)).astype(np.int32)
     r = orc.moe_route(idx, E)
-    rows = _where_loop_rows(idx, E)
+    rows = _stable_sort_rows(idx, E)
     assert list(zip(r["row_token"].tolist(), r["row_slot"].tolist())) == rows
     assert np.array_equal(np.diff(r["offsets"]), np.bincount(idx.ravel(), minlength=E))
     assert r["offsets"][0] == 0 and r["offsets"][-1] == T * topk
@@ -500,29 +502,35 @@ def test_moe_quant_scatter_is_gather_then_quant(orc, fmt):
     assert np.array_equal(q, qg) and np.array_equal(s.view(np.uint32), sg.view(np.uint32))
 
 
-def test_moe_combine_matches_expert_loop(orc):
-    """The token-major combine against the pages' expert-major loop
-    y[idx] += expert(x[idx]) * weights[idx, top] (Admin guide 6.4), both in
-    float64, where expert e is a fixed random linear map: the combine reads
-    the expert outputs laid out in routed-row order."""
+def test_moe_combine_matches_pairwise_sum(orc):
+    """The combine (Admin guide 6.4: every expert output weighted by the
+    routing weight of its (token, slot) and added into that token's output)
+    against a formulation that never looks at the route: for each (token,
+    slot) pair the output of its expert on its token is recomputed from
+    scratch, rounded to bf16 like the stored expert outputs, weighted, and
+    scattered into the token with np.add.at, all in float64.  Expert e is a
+    fixed random linear map; the combine itself reads the expert outputs in
+    routed-row order through the route's row_of."""
     rng = np.random.default_rng(31)
     T, topk, E, D, N = 50, 4, 7, 16, 24
     idx = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
     w = rng.uniform(0.05, 1.0, (T, topk)).astype(np.float32)
     x = rng.standard_normal((T, D))
     W = rng.standard_normal((E, D, N))
+
+    def bf16_round(a):
+        return torch.from_numpy(a).float().to(torch.bfloat16).double().numpy()
+
     r = orc.moe_route(idx, E)
     R = int(r["offsets"][-1])
     experts = np.repeat(np.arange(E), np.diff(r["offsets"]))
     out = np.stack([x[r["row_token"][i]] @ W[experts[i]] for i in range(R)])
     out_bits = inputs.bf16_bits(torch.from_numpy(out).float().to(torch.bfloat16))
-    out_bf = torch.from_numpy(out_bits.view(np.int16)).view(torch.bfloat16).double().numpy()
     y = orc.moe_combine(out_bits, w, r["row_of"])
+    tok = np.repeat(np.arange(T), topk)
+    pair_out = bf16_round(np.stack([x[t] @ W[e] for t, e in zip(tok, idx.reshape(-1))]))
     ref = np.zeros((T, N))
-    for e in range(E):
-        tok, top = np.nonzero(idx == e)
-        rows = r["row_of"][tok, top]
-        ref[tok] += out_bf[rows] * w[tok, top][:, None].astype(np.float64)
+    np.add.at(ref, tok, pair_out * w.reshape(-1, 1).astype(np.float64))
     assert np.allclose(y, ref, rtol=1e-14, atol=1e-14)
 
 
