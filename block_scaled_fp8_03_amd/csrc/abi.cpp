@@ -154,8 +154,8 @@ int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* 
   if (na < 0 || nbe < 0 || nb < 0 || nc < 0 || mul(R + 256, K) >= kLimit32 ||
       mul(N + 256, K) >= kLimit32 || mul(nc, 4) < 0)
     return FP8BS_ERR_SHAPE;
-  // each of the two launch grids is at most (R / 64 + 2 E) * ceil(N / 256) + 7 workgroups
-  if (mul(R / 64 + 2 * E, cdiv(N, 256)) > kLimitInt - 7) return FP8BS_ERR_SHAPE;
+  // the launch grid is at most (R / 256 + 2 E) * ceil(N / 256) + 16 workgroups
+  if (mul(R / 64 + 2 * E, cdiv(N, 256)) > kLimitInt - 16) return FP8BS_ERR_SHAPE;
   if (nc == 0 || E == 0) return FP8BS_OK;
   if (!a || !a_s || !b || !b_s || !offsets || !c) return FP8BS_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16) || !aligned(a_s, 4) ||

@@ -19,7 +19,6 @@
 // result lane l, register r is D[4 (l / 16) + r][l % 16].
 #include <algorithm>
 #include <cstdint>
-#include <mutex>
 
 #include "device_common.h"
 #include "launch.h"
@@ -137,9 +136,8 @@ struct GemmParams {
   int rows;               // M (dense) or R (MoE)
   int N, K;
   int E;                  // MoE experts
-  int num_m;              // dense: m tiles; MoE: upper bound on (expert, m-tile) pairs
+  int num_m;              // dense: m tiles
   int num_n;              // n tiles
-  int moe_lo, moe_hi;     // MoE: this launch takes the experts with moe_lo < rows <= moe_hi
   int n0;                 // dense: first output column of this launch's tiles (a multiple of 128)
 };
 
@@ -246,10 +244,23 @@ __device__ __forceinline__ void store_c_tile_bf16(uint8_t* smem, const v4f (&acc
   }
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool MOE,
-          int OCC, bool E8 = false>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))
-gemm_tile_kernel(GemmParams p) {
+// LDS bytes of one tile configuration (stages, a_s chunk buffers, dummy area).
+template <int BM, int BN, int ST, int NW, bool ASCH>
+constexpr int tile_lds_bytes() {
+  return ST * (BM * 128 + BN * 128 + (ASCH ? 0 : NW * 256) + NW * 256) + (ASCH ? 2 * NW * 1024 : 0) +
+         ((ASCH && ST > 2) ? 256 : 0);
+}
+
+// One BM x BN tile of C: rows [m_base, m_base + BM) of A (results stored
+// for rows < m_end) times rows [n_base, n_base + BN) of the weight B with
+// block scales Bs.  `smem` is the workgroup's LDS, at least
+// tile_lds_bytes<BM, BN, ST, NW, ASCH>() bytes, 1024-byte aligned.  Every
+// wave of the workgroup calls it with the same arguments.
+// NT_B: the weight DMA carries the non-temporal hint.
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, bool NT_B,
+          bool E8>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, int m_base, int m_end,
+                                          int n_base, const uint8_t* B, const float* Bs) {
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static_assert(WAVES_M * WAVES_N == NW && (NW == 4 || NW == 8), "4 or 8 waves per workgroup");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range lies in one weight block");
@@ -264,8 +275,7 @@ gemm_tile_kernel(GemmParams p) {
   constexpr int ASC = ASCH ? NW * 256 / BM : 1;                       // K blocks per a_s chunk
   static_assert(!ASCH || (ASC % 4 == 0 && ASC >= ST - 1), "a_s chunk shape");
   constexpr int CHUNK_BYTES = ASCH ? NW * 1024 : 0;
-  constexpr int DUMMY_BYTES = (ASCH && ST > 2) ? 256 : 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 2 * CHUNK_BYTES + DUMMY_BYTES];
+  static_assert(tile_lds_bytes<BM, BN, ST, NW, ASCH>() <= 160 * 1024, "LDS");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,107 +283,6 @@ gemm_tile_kernel(GemmParams p) {
   const int K = p.K, N = p.N;
   const int nkb = K / 128;
   const int nbn = (N + 127) / 128;
-
-  // ---- which tile
-  int m_base, m_end, n_base;
-  const uint8_t* B;
-  const float* Bs;
-  {
-    const int total = gridDim.x;
-    const int t = xcd_remap(blockIdx.x, total);
-    if (!MOE) {
-      // Groups of GM m-tiles sweep across n (consecutive tiles share B or A).
-      constexpr int GM = 4;
-      const int group = GM * p.num_n;
-      const int gid = t / group, first_m = gid * GM;
-      const int gsz = min(p.num_m - first_m, GM);
-      const int in = t % group;
-      const int mt = first_m + in % gsz, nt = in / gsz;
-      m_base = mt * BM;
-      m_end = p.rows;
-      n_base = p.n0 + nt * BN;
-      B = p.b;
-      Bs = p.b_s;
-    } else {
-      // The grid is an upper bound on the tile count.  Every workgroup counts
-      // the real (expert, m-tile) pairs from the device offsets, and the real
-      // tiles -- n-minor, so consecutive tiles share an expert's activation
-      // rows -- are dealt to the XCDs as equal contiguous ranges: each XCD
-      // reads a slab of activations once for all its n tiles, and an expert's
-      // weight on the one or two XCDs that hold its m tiles (measured on the
-      // 4096-token MoE: down-projection 1.40-1.49 -> 1.30 ms; an n-major order
-      // made every XCD re-read all activation rows).  The host pads the grid
-      // by 7 so that the eight ranges cover every real tile.
-      int total_m = 0;
-      for (int e0 = 0; e0 < p.E; e0 += 64) {
-        const int ee = e0 + lane;
-        int cnt = 0;
-        if (ee < p.E) {
-          int lo = p.offsets[ee], hi = p.offsets[ee + 1];
-          lo = min(max(lo, 0), p.rows);
-          hi = min(max(hi, lo), p.rows);
-          const int n_rows = hi - lo;
-          cnt = (n_rows > p.moe_lo && n_rows <= p.moe_hi) ? (n_rows + BM - 1) / BM : 0;
-        }
-        int incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int v = __shfl_up(incl, d);
-          if (lane >= d) incl += v;
-        }
-        total_m += __shfl(incl, 63);
-      }
-      total_m = __builtin_amdgcn_readfirstlane(total_m);
-      const int real = total_m * p.num_n;
-      const int per_xcd = (real + 7) / 8;
-      const int bx = blockIdx.x;
-      const int tt = (bx % 8) * per_xcd + bx / 8;
-      if (bx / 8 >= per_xcd || tt >= real) return;         // no real tile (uniform)
-      const int nt = tt % p.num_n, gm = tt / p.num_n;
-      int e = -1, mt = 0;
-      {
-        int before = 0;                         // m tiles of experts < chunk start
-        for (int e0 = 0; e0 < p.E && e < 0; e0 += 64) {
-          const int ee = e0 + lane;
-          int cnt = 0;
-          if (ee < p.E) {
-            int lo = p.offsets[ee], hi = p.offsets[ee + 1];
-            lo = min(max(lo, 0), p.rows);
-            hi = min(max(hi, lo), p.rows);
-            const int n_rows = hi - lo;
-            cnt = (n_rows > p.moe_lo && n_rows <= p.moe_hi) ? (n_rows + BM - 1) / BM : 0;
-          }
-          // inclusive prefix sum over the wave
-          int incl = cnt;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-          }
-          const int excl = before + incl - cnt;
-          const bool mine = (ee < p.E) && gm >= excl && gm < excl + cnt;
-          const unsigned long long ball = __ballot(mine);
-          if (ball) {
-            const int src = __ffsll((long long)ball) - 1;
-            e = __shfl(ee, src);
-            mt = gm - __shfl(excl, src);
-          }
-          before += __shfl(incl, 63);
-        }
-      }
-      e = __builtin_amdgcn_readfirstlane(e);
-      mt = __builtin_amdgcn_readfirstlane(mt);
-      if (e < 0) return;                        // past the last real tile (uniform)
-      int lo = p.offsets[e], hi = p.offsets[e + 1];
-      lo = min(max(lo, 0), p.rows);
-      hi = min(max(hi, lo), p.rows);
-      m_base = __builtin_amdgcn_readfirstlane(lo + mt * BM);
-      m_end = __builtin_amdgcn_readfirstlane(hi);
-      n_base = nt * BN;
-      B = p.b + (int64_t)e * N * K;
-      Bs = p.b_s + (int64_t)e * nbn * nkb;
-    }
-  }
 
   // ---- DMA sources.  Load i of this wave covers the 8 rows 8*(NW*i+wave)
   // .. +7 of the tile; lane l takes row l/8 of those and the logical chunk
@@ -408,11 +317,11 @@ gemm_tile_kernel(GemmParams p) {
       dma_b128s(a_rsrc, base + i * NW * 1024, a_voff + i * rowstep, koff);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      // The small-expert MoE tiles (at most 64 rows per expert, one m tile)
-      // read each expert's weight exactly once: non-temporal DMA (measured on
-      // the 4096-token MoE: up 1062 -> 1030 us, down 1169 -> 1124 us; the
+      // NT_B: the weight is read exactly once (the small-expert MoE tiles:
+      // at most 64 rows per expert, one m tile): non-temporal DMA (measured
+      // on the 4096-token MoE: up 1062 -> 1030 us, down 1169 -> 1124 us; the
       // same hint on the 256-row tiles of single-tile experts did not help).
-      if (MOE && BM == 64) dma_b128s_nt(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
+      if (NT_B) dma_b128s_nt(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
       else dma_b128s(b_rsrc, base + A_BYTES + i * NW * 1024, b_voff + i * rowstep, koff);
     }
     if (ASCH) {
@@ -551,6 +460,176 @@ gemm_tile_kernel(GemmParams p) {
       }
     }
   }
+}
+
+// Dense GEMM: one tile per workgroup.  OCC workgroups share a CU (register
+// budget set for OCC * NW / 4 waves per SIMD).
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool OUT_F32, int OCC,
+          bool E8 = false>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC * NW / 4, OCC * NW / 4)))
+gemm_tile_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<BM, BN, ST, NW, ASCH>()];
+  // Groups of GM m-tiles sweep across n (consecutive tiles share B or A).
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GM = 4;
+  const int group = GM * p.num_n;
+  const int gid = t / group, first_m = gid * GM;
+  const int gsz = min(p.num_m - first_m, GM);
+  const int in = t % group;
+  const int mt = first_m + in % gsz, nt = in / gsz;
+  gemm_tile<BM, BN, WM, WN, ST, NW, SW, ASCH, OUT_F32, false, E8>(p, smem, mt * BM, p.rows,
+                                                                   p.n0 + nt * BN, p.b, p.b_s);
+}
+
+// ----------------------------------------------------------------------------
+// Grouped MoE GEMM: both expert classes in one launch
+// ----------------------------------------------------------------------------
+// Experts are classed by their row count.  Experts with more than kMoeSplit
+// rows are dense GEMMs in their own right and take the 256 x 256 tile of the
+// dense path (bound by the matrix cores); the others -- most experts under
+// skewed routing, and most of the weight bytes -- take one 64 x 256 tile per
+// weight slice, three LDS stages, the weight read once with the
+// non-temporal hint (bound by HBM).  Both shapes run in eight-wave
+// workgroups of one kernel, so the two classes share the CUs in one grid:
+// while some CUs multiply the large experts, the others stream the small
+// experts' weights.
+//
+// Schedule.  The grid is an upper bound on the tile count, sized on the host
+// from R and E alone.  Every workgroup counts the real m tiles of each class
+// from the device offsets (wave prefix sums over the experts).  Each class's
+// tiles -- (expert, m tile) pairs in expert order, n-minor, so consecutive
+// tiles share an expert's activation rows -- are cut into eight contiguous
+// parts, one per XCD (workgroups are dealt to the XCDs round-robin, so
+// workgroup b runs on XCD b % 8 as its (b / 8)-th): an XCD reads an
+// activation slab once for all its n tiles and an expert's weight on the one
+// or two XCDs that hold its m tiles.  Within an XCD the large tiles are
+// spread evenly over the first L + S * kMoeMix / 256 positions of its
+// sequence and the small tiles fill the rest, so the long compute-bound tiles
+// are all dispatched before the sequence ends in short streaming tiles.
+constexpr int kMoeSplit = 64;
+constexpr int kMoeMix = 160;
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// m tiles of an expert with n_rows rows in class `large`.
+__device__ __forceinline__ int class_mtiles(int n_rows, bool large) {
+  return large ? (n_rows > kMoeSplit ? (n_rows + 255) / 256 : 0) : ((n_rows > 0 && n_rows <= kMoeSplit) ? 1 : 0);
+}
+
+// Rows of the experts e0 + 64 j + lane (j < 4), ranges clamped to [0, R]
+// (0 past the last expert).  The eight offset loads are issued together:
+// every workgroup runs this before its tile while its CU waits, so it costs
+// one memory round trip per 256 experts instead of one per 64.
+__device__ __forceinline__ void expert_rows4(const GemmParams& p, int e0, int lane, int (&rows)[4]) {
+  int lo[4], hi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ee = min(e0 + 64 * j + lane, p.E - 1);
+    lo[j] = p.offsets[ee];
+    hi[j] = p.offsets[ee + 1];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int l = min(max(lo[j], 0), p.rows);
+    rows[j] = e0 + 64 * j + lane < p.E ? min(max(hi[j], l), p.rows) - l : 0;
+  }
+}
+
+template <bool ASCH, bool OUT_F32>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+moe_gemm_kernel(GemmParams p) {
+  constexpr int LB = tile_lds_bytes<256, 256, 2, 8, ASCH>(), SB = tile_lds_bytes<64, 256, 3, 8, ASCH>();
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LB > SB ? LB : SB];
+  const int lane = threadIdx.x & 63;
+  const int nn = p.num_n;
+
+  // real m tiles of each class (the first 256 experts' row counts are kept)
+  int rows0[4];
+  expert_rows4(p, 0, lane, rows0);
+  int ml = 0, ms = 0;
+  for (int e0 = 0; e0 < p.E; e0 += 256) {
+    int rows[4];
+    if (e0 == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rows[j] = rows0[j];
+    } else {
+      expert_rows4(p, e0, lane, rows);
+    }
+    int cl = 0, cs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cl += class_mtiles(rows[j], true);
+      cs += class_mtiles(rows[j], false);
+    }
+    ml += __shfl(wave_incl_scan(cl, lane), 63);
+    ms += __shfl(wave_incl_scan(cs, lane), 63);
+  }
+  const int64_t L = (int64_t)__builtin_amdgcn_readfirstlane(ml) * nn;
+  const int64_t S = (int64_t)__builtin_amdgcn_readfirstlane(ms) * nn;
+
+  // this XCD's parts of both lists and this workgroup's place in its sequence
+  const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int64_t l0 = L * x / 8, lx = L * (x + 1) / 8 - l0;
+  const int64_t s0 = S * x / 8, sx = S * (x + 1) / 8 - s0;
+  if (k >= lx + sx) return;                               // no real tile (uniform)
+  const int64_t pl = lx + sx * kMoeMix / 256;             // positions holding the large tiles
+  bool large;
+  int64_t idx;
+  if (k < pl) {
+    const int64_t before = (int64_t)k * lx / pl;          // large tiles at positions < k
+    large = ((int64_t)(k + 1) * lx / pl) > before;
+    idx = large ? l0 + before : s0 + (k - before);
+  } else {
+    large = false;
+    idx = s0 + (k - lx);
+  }
+  const int nt = (int)(idx % nn), gm = (int)(idx / nn);
+
+  // the expert and m tile of class m tile gm: experts in index order, so
+  // expert e0 + 64 j + lane comes after all of chunk j - 1 of its 256
+  int e = -1, mt = 0, before = 0;
+  for (int e0 = 0; e0 < p.E && e < 0; e0 += 256) {
+    int rows[4];
+    if (e0 == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rows[j] = rows0[j];
+    } else {
+      expert_rows4(p, e0, lane, rows);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cnt = class_mtiles(rows[j], large);
+      const int incl = wave_incl_scan(cnt, lane);
+      const int excl = before + incl - cnt;
+      const unsigned long long ball = __ballot(gm >= excl && gm < excl + cnt);
+      if (ball && e < 0) {
+        const int src = __ffsll((long long)ball) - 1;
+        e = e0 + 64 * j + src;
+        mt = gm - __shfl(excl, src);
+      }
+      before += __shfl(incl, 63);
+    }
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  if (e < 0) return;                                      // unreachable for valid offsets (uniform)
+  const int lo = __builtin_amdgcn_readfirstlane(min(max(p.offsets[e], 0), p.rows));
+  const int hi = __builtin_amdgcn_readfirstlane(min(max(p.offsets[e + 1], lo), p.rows));
+  const int nbn = (p.N + 127) / 128, nkb = p.K / 128;
+  const uint8_t* B = p.b + (int64_t)e * p.N * p.K;
+  const float* Bs = p.b_s + (int64_t)e * nbn * nkb;
+  if (large)
+    gemm_tile<256, 256, 128, 64, 2, 8, 2, ASCH, OUT_F32, false, false>(p, smem, lo + mt * 256, hi, nt * 256, B, Bs);
+  else
+    gemm_tile<64, 256, 64, 32, 3, 8, 2, ASCH, OUT_F32, true, false>(p, smem, lo, hi, nt * 256, B, Bs);
 }
 
 // ----------------------------------------------------------------------------
@@ -1346,23 +1425,23 @@ w8a16_tile_kernel(GemmParams p) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, bool MOE, int OCC, bool E8>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool ASCH, int OCC, bool E8>
 void launch_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   if (out_f32)
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, MOE, OCC, E8><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, true, OCC, E8><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
   else
-    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, MOE, OCC, E8><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
+    gemm_tile_kernel<BM, BN, WM, WN, ST, NW, SW, ASCH, false, OCC, E8><<<dim3(grid), dim3(NW * 64), 0, stream>>>(p);
 }
 
 // Chunked a_s loads (16 bytes per lane) need every row of a_s to start on a
 // 16-byte boundary.
-template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, bool MOE, int OCC = 1, bool E8 = false>
+template <int BM, int BN, int WM, int WN, int ST, int NW, int SW, int OCC = 1, bool E8 = false>
 hipError_t run_tile(const GemmParams& p, bool out_f32, int grid, hipStream_t stream) {
   const bool chunked = (p.K / 128) % 4 == 0 && ((uintptr_t)p.a_s & 15) == 0;
   if (chunked)
-    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, MOE, OCC, E8>(p, out_f32, grid, stream);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, true, OCC, E8>(p, out_f32, grid, stream);
   else
-    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, MOE, OCC, E8>(p, out_f32, grid, stream);
+    launch_tile<BM, BN, WM, WN, ST, NW, SW, false, OCC, E8>(p, out_f32, grid, stream);
   return hipGetLastError();
 }
 
@@ -1439,11 +1518,11 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
     if (tiles(128, 128) >= cus / 2) {
       p.num_m = (int)((M + 127) / 128);
       p.num_n = (int)((N + 127) / 128);
-      return run_tile<128, 128, 64, 64, 3, 4, 2, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
+      return run_tile<128, 128, 64, 64, 3, 4, 2, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
     }
     p.num_m = (int)((M + 63) / 64);
     p.num_n = (int)((N + 63) / 64);
-    return run_tile<64, 64, 32, 32, 3, 4, 2, false, 2, E8>(p, out_f32, p.num_m * p.num_n, stream);
+    return run_tile<64, 64, 32, 32, 3, 4, 2, 2, E8>(p, out_f32, p.num_m * p.num_n, stream);
   }
   p.num_m = (int)((M + BM - 1) / BM);
   p.num_n = (int)((N + BN - 1) / BN);
@@ -1462,7 +1541,7 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
     const double split_cost = (double)(full / cus) + (double)((tail_tiles + 2 * cus - 1) / (2 * cus)) * kTailCost;
     if (split_cost < (double)((T + cus - 1) / cus)) {
       p.num_n = n_main;
-      hipError_t e = run_tile<256, 256, 128, 64, 2, 8, 2, false, 1, E8>(p, out_f32, (int)full, stream);
+      hipError_t e = run_tile<256, 256, 128, 64, 2, 8, 2, 1, E8>(p, out_f32, (int)full, stream);
       if (e != hipSuccess) return e;
       GemmParams q = p;
       q.n0 = n_main * BN;
@@ -1474,10 +1553,10 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
       // one workgroup per CU of 128 x 256 tiles (eight waves, three stages):
       // prefill 513.6 -> 500.9 us, N = 18000 509.2 -> 493.9 us, ue8m0
       // prefill 468.3 -> 455.8 us.
-      return run_tile<128, 128, 64, 64, 2, 4, 2, false, 2, E8>(q, out_f32, q.num_m * q.num_n, stream);
+      return run_tile<128, 128, 64, 64, 2, 4, 2, 2, E8>(q, out_f32, q.num_m * q.num_n, stream);
     }
   }
-  return run_tile<256, 256, 128, 64, 2, 8, 2, false, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
+  return run_tile<256, 256, 128, 64, 2, 8, 2, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
 }
 
 hipError_t launch_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c,
@@ -1493,42 +1572,6 @@ hipError_t launch_gemm_ue8m0(const void* a, const float* a_s, const void* b, con
   return dense_gemm<true>(a, a_s, b, b_s, c, M, N, K, out_f32, stream);
 }
 
-namespace {
-
-// A second stream and two events per device, for a launch made of two
-// independent kernels that should share the CUs: the caller's stream records
-// `fork`, the side stream waits on it and takes one kernel and records
-// `join`, and the caller's stream takes the other kernel and waits on
-// `join` -- so on the caller's stream the pair is ordered like one launch
-// (and a stream capture records it as a fork and a join).  Created on first
-// use and kept for the process, at the default priority; the mutex keeps the
-// record/wait pairs of concurrent host threads from interleaving.
-struct SideStream {
-  std::mutex mu;
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-
-SideStream* side_stream() {
-  static SideStream table[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream& x = table[dev];
-  std::lock_guard<std::mutex> g(x.mu);
-  if (!x.s && !x.failed) {
-    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
-      x.failed = true;              // fall back to one stream from now on
-      (void)hipGetLastError();
-    }
-  }
-  return x.failed ? nullptr : &x;
-}
-
-}  // namespace
-
 hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
                            const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N,
                            int64_t K, bool out_f32, hipStream_t stream) {
@@ -1536,59 +1579,24 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   GemmParams p{};
   p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
   p.offsets = offsets; p.rows = (int)R; p.N = (int)N; p.K = (int)K; p.E = (int)E;
-  // Experts are split by their row count.  Experts with more than
-  // kMoeSplit rows are dense GEMMs in their own right and run on the
-  // 256 x 256 tile of the dense path; the rest -- most experts under skewed
-  // routing, and most of the weight bytes -- stream their weights through
-  // 64-row tiles with three LDS stages.  Each launch finds its experts from
-  // the device offsets; the grids are upper bounds on its tile count
-  // (tiles past the end exit at once).
-  constexpr int kMoeSplit = 64;
-  // The two classes run side by side (the small experts on the side stream):
-  // under skewed routing one is bound by the matrix cores and the other by
-  // HBM, and each grid's last round of workgroups is only partly full, so
-  // the CUs are better used when the two grids share them than one after the
-  // other.
-  SideStream* ss = side_stream();
-  std::unique_lock<std::mutex> lock;
-  hipStream_t small_stream = stream;
-  if (ss) {
-    lock = std::unique_lock<std::mutex>(ss->mu);
-    hipError_t e = hipEventRecord(ss->fork, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
-    if (e != hipSuccess) return e;
-    small_stream = ss->s;
+  p.num_n = (int)((N + 255) / 256);
+  // Upper bounds on each class's m tiles: the large experts' sum of
+  // ceil(rows / 256) <= R / 256 + (number of such experts), with at most
+  // R / (kMoeSplit + 1) of them; one small tile per expert with rows.
+  const int64_t ml = R / 256 + std::min<int64_t>(E, R / (kMoeSplit + 1));
+  const int64_t ms = std::min<int64_t>(E, R);
+  // each XCD's part of a class list is at most ceil(tiles / 8)
+  const int64_t grid = 8 * ((ml * p.num_n + 7) / 8 + (ms * p.num_n + 7) / 8);
+  const bool chunked = (K / 128) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
+  const dim3 g((unsigned)grid), blk(512);
+  if (chunked) {
+    if (out_f32) moe_gemm_kernel<true, true><<<g, blk, 0, stream>>>(p);
+    else moe_gemm_kernel<true, false><<<g, blk, 0, stream>>>(p);
+  } else {
+    if (out_f32) moe_gemm_kernel<false, true><<<g, blk, 0, stream>>>(p);
+    else moe_gemm_kernel<false, false><<<g, blk, 0, stream>>>(p);
   }
-  hipError_t err = hipSuccess;
-  {
-    constexpr int BM = 256, BN = 256;
-    GemmParams q = p;
-    q.moe_lo = kMoeSplit;
-    q.moe_hi = INT32_MAX;
-    // sum over experts with > kMoeSplit rows of ceil(rows / BM)
-    //   <= R / BM + (number of such experts) <= R / BM + R / (kMoeSplit + 1)
-    q.num_m = (int)(R / BM + std::min<int64_t>(E, R / (kMoeSplit + 1)));
-    q.num_n = (int)((N + BN - 1) / BN);
-    if (q.num_m > 0) err = run_tile<BM, BN, 128, 64, 2, 8, 2, true>(q, out_f32, q.num_m * q.num_n + 7, stream);
-  }
-  if (err == hipSuccess) {
-    constexpr int BM = 64, BN = 256;
-    GemmParams q = p;
-    q.moe_lo = 0;
-    q.moe_hi = kMoeSplit;
-    // sum over experts with <= kMoeSplit rows of ceil(rows / BM) <= E * ceil(kMoeSplit / BM)
-    q.num_m = (int)(E * ((kMoeSplit + BM - 1) / BM));
-    q.num_n = (int)((N + BN - 1) / BN);
-    err = run_tile<BM, BN, 64, 64, 3, 4, 2, true>(q, out_f32, q.num_m * q.num_n + 7, small_stream);
-  }
-  if (ss) {
-    // join even after a failed launch, so the side stream never runs ahead
-    // of later work on the caller's stream
-    hipError_t e = hipEventRecord(ss->join, ss->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
-    if (err == hipSuccess) err = e;
-  }
-  return err;
+  return hipGetLastError();
 }
 
 // The grid of p.num_m x p.num_n tiles (columns from p.n0 on).

@@ -12,10 +12,9 @@
  *     1 x 128 block along K, weights one per 128 x 128 block.  A scale is the
  *     dequantisation multiplier: real value = decode(code) * scale.
  *   - The caller owns all memory.  The library never allocates or frees
- *     device memory.  Its only process-wide state is a per-device cache of
- *     the compute-unit count and, for fp8bs_moe_gemm, one extra stream and
- *     two events per device, created on first use (under a mutex) and kept
- *     until the process ends.  It is safe to call from several host threads.
+ *     device memory, creates no streams or events, and keeps no state
+ *     between calls beyond a per-device cache of the compute-unit count.  It
+ *     is safe to call from several host threads.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream) on the
  *     current HIP device; all pointers must be device (or managed) memory of
  *     that device.
@@ -169,14 +168,13 @@ int fp8bs_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
  *                 left untouched
  *   R, E >= 0 (either 0 = no-op), N >= 0, K >= 128 with K % 128 == 0;
  *   (R + 256) * K < 2^32 and (N + 256) * K < 2^32.
- * Runs as two launches: experts with more than 64 rows on the 256 x 256
- * tiles of fp8bs_gemm (on `stream`), the others on 64 x 256 tiles, on a
- * second stream the library keeps per device (default priority) that waits
- * for `stream` before it starts, and that `stream` waits for afterwards: on
- * `stream` the call is ordered like a single launch, and a stream capture of
- * `stream` records it as a fork and a join.  Both grids are sized on the host
- * from R and E alone (each finds its experts from the device offsets);
- * experts with no rows cost (almost) nothing.
+ * One launch on `stream`: experts with more than 64 rows run on the 256 x 256
+ * tiles of fp8bs_gemm, the others on 64 x 256 tiles that stream the weight
+ * once, the two kinds of tiles sharing the grid.  The grid is sized on the
+ * host from R and E alone (each workgroup finds its tile from the device
+ * offsets, so no device-to-host copy is needed); experts with no rows cost
+ * nothing.  Accuracy as fp8bs_gemm for M > 64 (both tile kinds use the FP8
+ * matrix instruction).
  */
 int fp8bs_moe_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
                    const int32_t* offsets, void* c, int64_t R, int64_t E, int64_t N, int64_t K,

@@ -2,9 +2,9 @@
 CPU oracle (binary64), through the C ABI.  Bar, element-wise:
 |gpu - ref| <= 1e-2 |ref| + 1e-3, on the float32 output and on the bf16 output.
 Small shapes are compared in full (several tiles, ragged M and N tails); the
-full-size workloads are compared in full where the oracle is quick (decode)
-and on sampled points elsewhere (whole rows, whole columns, tile corners and
-random points), in the launch configuration the benchmark times."""
+full-size workloads (decode, prefill up and down, the two GEMMs of the ue8m0
+workload, the grouped MoE up and down over all 256 experts) are compared in
+full, in the launch configuration the benchmark times."""
 import numpy as np
 import pytest
 import torch
@@ -239,17 +239,51 @@ def test_gemm_decode_full():
 
 
 def test_gemm_prefill_up():
-    full_size_case(3, 4096, 18432, 7168, inputs.seed_for(3, 0), inputs.seed_for(3, 1))
+    """The prefill linear x [4096, 7168] . W [18432, 7168]^T, every output."""
+    full_size_case(3, 4096, 18432, 7168, inputs.seed_for(3, 0), inputs.seed_for(3, 1), full=True)
 
 
 def test_gemm_prefill_down():
-    full_size_case(3, 4096, 7168, 18432, inputs.seed_for(3, 2), inputs.seed_for(3, 3))
+    """The prefill down-projection x [4096, 18432] . W [7168, 18432]^T, every output."""
+    full_size_case(3, 4096, 7168, 18432, inputs.seed_for(3, 2), inputs.seed_for(3, 3), full=True)
+
+
+def test_gemm_prefill_outliers_full():
+    """The prefill GEMM shape on activations with 1% x50 outliers, every
+    output: the FP8-MFMA tile path's bar carries the hardware term 2^-11 *
+    (oracle GEMM of the magnitudes), as the header's accuracy note states;
+    the count of outputs that miss the plain bar 1e-2 |ref| + 1e-3 is
+    printed and must stay a small fraction."""
+    M, N, K = 4096, 18432, 7168
+    x = inputs.normal_bf16((M, K), 1.0, inputs.seed_for(3, 40), outlier_frac=0.01, outlier_mult=50.0)
+    w = inputs.normal_bf16((N, K), 0.02, inputs.seed_for(3, 41))
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w))
+    del w
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), oracle.FMT_FP32)
+    qd, sd = fp8bs.act_quant(x.to(DEV), oracle.FMT_FP32)
+    c32 = fp8bs.fp8_gemm(qd, sd, to_dev_u8(b), to_dev_f32(b_s), torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(qd.view(torch.uint8).cpu().numpy(), a)
+    got = c32.cpu().numpy().astype(np.float64)
+    del c32
+    ref = oracle.gemm(a, a_s, b, b_s)
+    err = np.abs(got - ref)
+    del got
+    plain = 1e-2 * np.abs(ref) + 1e-3
+    del ref
+    miss = int(np.count_nonzero(~(err <= plain)))
+    mag = oracle.gemm(a & 0x7F, a_s, b & 0x7F, b_s)
+    over = int(np.count_nonzero(~(err <= plain + 2.0 ** -11 * mag)))
+    print(f"prefill outliers: {miss} of {err.size} outputs outside the plain bar, "
+          f"{over} outside the bar with the hardware term")
+    assert over == 0, "hardware-term bar"
+    assert miss / err.size < 1e-3, "plain bar"
 
 
 @pytest.mark.parametrize("N,K,tid", [(1536, 7168, 2), (16384, 512, 4)])
 def test_gemm_ue8m0_inputs(N, K, tid):
     full_size_case(5, 1024, N, K, inputs.seed_for(5, tid), inputs.seed_for(5, tid + 1),
-                   fmt=oracle.FMT_UE8M0)
+                   fmt=oracle.FMT_UE8M0, full=True)
 
 
 # --------------------------------------------------------------------- MoE
@@ -292,13 +326,68 @@ def test_moe_small(counts, N, K):
     assert_close(run_moe(a, a_s, b, b_s, off, torch.bfloat16), ref, f"moe{counts} bf16")
 
 
+def _moe_operands_from_counts(counts, N, K, seed):
+    """Oracle-quantised operands of a grouped GEMM with the given per-expert
+    row counts; each expert's weight is quantised on its own (its block rows
+    do not cross into the next expert's when N % 128 != 0)."""
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    x = inputs.normal_bf16((R, K), 1.0, seed)
+    a, a_s = oracle.act_quant(inputs.bf16_bits(x), 0)
+    w = inputs.normal_bf16((E * N, K), 0.02, seed + 1)
+    per = [oracle.weight_quant(inputs.bf16_bits(w[e * N:(e + 1) * N])) for e in range(E)]
+    b = np.stack([q for q, _ in per])
+    b_s = np.stack([sc for _, sc in per])
+    return a, a_s, b, b_s, off
+
+
+@pytest.mark.parametrize("name,E,N,K,seed", [
+    ("mixed, E > 4 x 64", 300, 512, 256, 1),   # both classes; expert scan over five 64-lane chunks
+    ("small only", 17, 768, 384, 2),          # every expert <= 64 rows
+    ("large only", 5, 300, 128, 3),           # every expert > 64 rows, ragged N
+    ("one row", 1, 256, 128, 4),
+    ("few tiles", 9, 256, 128, 5),            # fewer tiles than XCDs in a class
+])
+def test_moe_schedule(name, E, N, K, seed):
+    """The one-launch schedule of both expert classes (tiles of each class
+    cut into eight contiguous parts, the large tiles spread over the first
+    positions of each part): every expert's rows are computed exactly once,
+    compared in full with the oracle on float32 and bf16 outputs; rows no
+    expert owns stay untouched."""
+    rng = np.random.default_rng(seed)
+    if name.startswith("mixed"):
+        counts = np.where(rng.random(E) < 0.15, rng.integers(65, 700, E),
+                          np.where(rng.random(E) < 0.2, 0, rng.integers(1, 65, E)))
+    elif name == "small only":
+        counts = rng.integers(1, 65, E)
+    elif name == "large only":
+        counts = rng.integers(65, 700, E)
+    elif name == "one row":
+        counts = np.array([1])
+    else:
+        counts = np.array([0, 70, 3, 0, 0, 64, 65, 1, 0])
+    a, a_s, b, b_s, off = _moe_operands_from_counts(counts.astype(np.int64), N, K, 7000 + seed)
+    R = int(off[-1])
+    ref = oracle.moe_gemm(a, a_s, b, b_s, off)
+    offd = torch.from_numpy(off).to(DEV)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        c = torch.full((R + 3, N), float("nan"), dtype=out_dtype, device=DEV)
+        fp8bs.fp8bs_moe_gemm(to_dev_u8(a), to_dev_f32(a_s), to_dev_u8(b), to_dev_f32(b_s), offd, c[:R])
+        torch.cuda.synchronize()
+        got = c.float().cpu().numpy()
+        assert_close(got[:R], ref, f"moe schedule {name} {out_dtype}")
+        assert np.all(np.isnan(got[R:])), "rows past R written"
+
+
 @pytest.mark.parametrize("proj", ["up", "down"])
 def test_moe_full_size(proj):
     """The grouped MoE workload: 4096 tokens, 256 experts, top-8 Zipf(1.1)
     routing; up W [256, 2048, 7168] or down W [256, 7168, 2048].  Weights are
-    drawn on the device (torch generator), quantised by the library, and the
-    quantisation of the experts used below is checked bit-exact against the
-    oracle before their rows are compared."""
+    drawn on the device (torch generator) and quantised by the library, as in
+    the benchmark; the oracle quantises the same draw itself and the two are
+    checked bit-exact; then every output of every expert (float32 and bf16)
+    is compared with the oracle's grouped GEMM."""
     cfg = inputs.CONFIGS[4]
     E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
     N, K = (cfg["up"]["N"], cfg["up"]["K"]) if proj == "up" else (cfg["down"]["N"], cfg["down"]["K"])
@@ -314,27 +403,19 @@ def test_moe_full_size(proj):
     qd, sd = fp8bs.act_quant(x.to(DEV), 0)
     w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(4, 2 if proj == "up" else 3), DEV)
     bq, bsq = fp8bs.weight_quant(w)
-    c = fp8bs.moe_gemm(qd, sd, bq.view(E, N, K), bsq.view(E, N // 128, K // 128),
-                       torch.from_numpy(off).to(DEV), torch.float32)
+    offd = torch.from_numpy(off).to(DEV)
+    c32 = fp8bs.moe_gemm(qd, sd, bq.view(E, N, K), bsq.view(E, N // 128, K // 128), offd, torch.float32)
+    c16 = fp8bs.moe_gemm(qd, sd, bq.view(E, N, K), bsq.view(E, N // 128, K // 128), offd, torch.bfloat16)
     torch.cuda.synchronize()
     assert np.array_equal(qd.view(torch.uint8).cpu().numpy(), a)
-    counts = np.diff(off)
-    pick = sorted({0, int(np.argmax(counts)), int(np.argmin(counts)), E - 1, E // 2,
-                   int(np.argsort(counts)[E // 2])})
-    rng = np.random.default_rng(11)
-    for e in pick:
-        r0, r1 = int(off[e]), int(off[e + 1])
-        if r1 == r0:
-            continue
-        we = w[e * N:(e + 1) * N].cpu()
-        be, bse = oracle.weight_quant(inputs.bf16_bits(we))
-        assert np.array_equal(bq[e * N:(e + 1) * N].view(torch.uint8).cpu().numpy(), be)
-        assert np.array_equal(bsq.view(E, N // 128, K // 128)[e].cpu().numpy().view(np.uint32),
-                              bse.view(np.uint32))
-        rows = np.concatenate([np.repeat(np.arange(r0, r1), 3), rng.integers(r0, r1, 2000)])
-        cols = np.concatenate([rng.integers(0, N, 3 * (r1 - r0)), rng.integers(0, N, 2000)])
-        rows = np.concatenate([rows, np.full(N, r0), np.full(N, r1 - 1)])
-        cols = np.concatenate([cols, np.arange(N), np.arange(N)])
-        ref = oracle.gemm_points(a[r0:r1], a_s[r0:r1], be, bse, rows - r0, cols)
-        rt, ct = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
-        assert_close(c[rt, ct].cpu().numpy(), ref, f"moe {proj} expert {e} ({r1 - r0} rows)")
+    b, b_s = oracle.weight_quant(inputs.bf16_bits(w.cpu()))
+    del w
+    assert np.array_equal(bq.view(torch.uint8).cpu().numpy(), b), "weight_quant codes"
+    assert np.array_equal(bsq.cpu().numpy().view(np.uint32), b_s.view(np.uint32)), "weight_quant scales"
+    del bq, bsq
+    # expert e's rows of the [E*N, K] weight are its [N, K] weight; its block
+    # rows are scale rows e*N/128 ..
+    ref = oracle.moe_gemm(a, a_s, b.reshape(E, N, K), b_s.reshape(E, N // 128, K // 128), off)
+    del b, b_s
+    assert_close(c32.cpu().numpy(), ref, f"moe {proj} f32 (all {E} experts)")
+    assert_close(c16.float().cpu().numpy(), ref, f"moe {proj} bf16 (all {E} experts)")

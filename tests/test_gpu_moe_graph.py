@@ -1,10 +1,9 @@
-"""Stream ordering of the grouped MoE GEMM.  The call runs its two expert
-classes side by side: experts with more than 64 rows on the caller's stream,
-the others on a second stream the library forks from the caller's stream and
-joins back with events.  These tests check that ordering from the outside: a
-consumer enqueued on the caller's stream right after the call sees the whole
-output, and a graph captured from the call replays to the same bytes as the
-eager call, several times, with eager work and synchronisation between the
+"""Stream ordering of the grouped MoE GEMM.  The call is one launch on the
+caller's stream that runs both expert classes (experts with more than 64 rows
+and the others).  These tests check that from the outside: a consumer
+enqueued on the caller's stream right after the call sees the whole output,
+and a graph captured from the call replays to the same bytes as the eager
+call, several times, with eager work and synchronisation between the
 replays.  Outputs are also checked against the oracle (binary64) with the GEMM
 bar |gpu - ref| <= 1e-2 |ref| + 1e-3."""
 import numpy as np
@@ -18,7 +17,7 @@ from gpu_util import DEV, assert_close, to_dev_f32, to_dev_u8
 
 pytestmark = pytest.mark.gpu
 
-# both expert classes present: <= 64 rows (side stream) and > 64 rows
+# both expert classes present: <= 64 rows and > 64 rows
 COUNTS = [3, 200, 64, 65, 0, 17, 300, 1, 40, 129]
 N, K = 384, 512
 
@@ -63,9 +62,8 @@ def test_moe_consumer_on_caller_stream(operands):
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_moe_graph_replays_match_eager(operands, out_dtype):
-    """A graph captured from the call (the side stream joins the capture
-    through the fork event) replays to the eager call's bytes, three times,
-    with eager work and synchronisation between the replays."""
+    """A graph captured from the call replays to the eager call's bytes,
+    three times, with eager work and synchronisation between the replays."""
     (a, a_s, b, b_s, off), ref, R = operands
     y_ref = torch.empty((R, N), dtype=out_dtype, device=DEV)
     fp8bs.fp8bs_moe_gemm(a, a_s, b, b_s, off, y_ref)
