@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_moe_route_workspace_size.argtypes = [I64, I64, I64]
     L.fp8bs_moe_route_workspace_size.restype = I64
     L.fp8bs_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
+    L.fp8bs_moe_route_noalloc.argtypes = [P, I64, I64, I64, P, P, P, P]
     L.fp8bs_moe_quant_scatter.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     L.fp8bs_moe_combine.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
     L.fp8bs_mla_absorb_key.argtypes = [P, I64, I64, P, P, P, I64, I64, I64, I64, I64, I, P]
@@ -231,6 +232,21 @@ def fp8bs_moe_route(indices: torch.Tensor, E: int, offsets: torch.Tensor, row_to
     _call("fp8bs_moe_route", _need(indices, (torch.int32,), "indices"), T, topk, E,
           _need(offsets, (torch.int32,), "offsets"), _need(row_token, (torch.int32,), "row_token"),
           _need(row_of, (torch.int32,), "row_of"), ws, nbytes, _stream(indices))
+
+
+def fp8bs_moe_route_noalloc(indices: torch.Tensor, E: int, offsets: torch.Tensor,
+                            row_token: torch.Tensor, row_of: torch.Tensor) -> None:
+    """fp8bs_moe_route without a workspace: the library's own device table
+    (no allocation; calls overlapping on one GPU race, see fp8bs.h)."""
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, topk]")
+    T, topk = indices.shape
+    if (tuple(offsets.shape) != (E + 1,) or tuple(row_token.shape) != (T * topk,)
+            or tuple(row_of.shape) != (T, topk)):
+        raise ValueError("offsets must be [E+1], row_token [T*topk] and row_of [T, topk]")
+    _call("fp8bs_moe_route_noalloc", _need(indices, (torch.int32,), "indices"), T, topk, E,
+          _need(offsets, (torch.int32,), "offsets"), _need(row_token, (torch.int32,), "row_token"),
+          _need(row_of, (torch.int32,), "row_of"), _stream(indices))
 
 
 def fp8bs_moe_quant_scatter(x: torch.Tensor, row_of: torch.Tensor, q: torch.Tensor, s: torch.Tensor,

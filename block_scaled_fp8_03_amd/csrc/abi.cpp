@@ -269,6 +269,24 @@ int fp8bs_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E, 
                                            workspace, (hipStream_t)stream));
 }
 
+int fp8bs_moe_route_noalloc(const int32_t* indices, int64_t T, int64_t topk, int64_t E,
+                            int32_t* offsets, int32_t* row_token, int32_t* row_of, void* stream) {
+  const int64_t need = fp8bs_moe_route_workspace_size(T, topk, E);
+  if (need < 0 || need > fp8bs::kRouteScratchBytes) return FP8BS_ERR_SHAPE;
+  const int64_t P = T * topk;
+  if (!offsets) return FP8BS_ERR_NULL;
+  if (P > 0 && (!indices || !row_token || !row_of)) return FP8BS_ERR_NULL;
+  if (!aligned(indices, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(row_of, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t ob = 4 * (E + 1), pb = 4 * P;
+  if (overlap(offsets, ob, indices, pb) || overlap(row_token, pb, indices, pb) ||
+      overlap(row_of, pb, indices, pb) || overlap(offsets, ob, row_token, pb) ||
+      overlap(offsets, ob, row_of, pb) || overlap(row_token, pb, row_of, pb))
+    return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_moe_route_noalloc(indices, T, topk, E, offsets, row_token, row_of,
+                                                   (hipStream_t)stream));
+}
+
 int fp8bs_moe_quant_scatter(const void* x_bf16, const int32_t* row_of, void* q_e4m3, float* s,
                             int64_t T, int64_t topk, int64_t R, int64_t K, int scale_fmt,
                             void* stream) {

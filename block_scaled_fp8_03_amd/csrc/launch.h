@@ -37,6 +37,12 @@ int64_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
 hipError_t launch_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E,
                             int32_t* offsets, int32_t* row_token, int32_t* row_of, void* workspace,
                             hipStream_t stream);
+// fp8bs_moe_route_noalloc: the count table in a file-scope device array of
+// kRouteScratchBytes per GPU instead of a caller workspace.
+constexpr int64_t kRouteScratchBytes = (int64_t)1 << 20;
+hipError_t launch_moe_route_noalloc(const int32_t* indices, int64_t T, int64_t topk, int64_t E,
+                                    int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                                    hipStream_t stream);
 hipError_t launch_moe_combine(const void* out, const float* w, const int32_t* row_of, void* y,
                               int64_t T, int64_t topk, int64_t R, int64_t N, bool out_f32,
                               hipStream_t stream);

@@ -14,6 +14,7 @@
 // (The expert inputs -- act_quant of each token written to its routed rows --
 // are the scatter variant of act_quant in quant.hip.)
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "launch.h"
@@ -271,6 +272,55 @@ hipError_t launch_moe_route(const int32_t* indices, int64_t T, int64_t topk, int
   moe_route_place_kernel<<<dim3(C), dim3(kRouteThreads), 0, stream>>>(indices, P, (int)topk, (int)E,
                                                                       hist, row_token, row_of);
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// route without a caller workspace
+// ----------------------------------------------------------------------------
+// For callers that cannot allocate (code under stream capture, serving loops,
+// harnesses that forbid allocation): the route's [chunks][E] count table
+// lives in a file-scope device array of kRouteScratchBytes instead of a
+// caller workspace.  Every GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, so
+// the array's device address is looked up once per device (with that device
+// current) and only that address is ever passed to a kernel.  The count
+// kernel overwrites every table entry the later kernels read, so nothing is
+// cleared between calls; two calls that overlap on one GPU share the table
+// and race.
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_moe_route_noalloc(const int32_t* indices, int64_t T, int64_t topk, int64_t E,
+                                    int32_t* offsets, int32_t* row_token, int32_t* row_of,
+                                    hipStream_t stream) {
+  if (moe_route_workspace_bytes(T, topk, E) > kRouteScratchBytes) return hipErrorInvalidValue;
+  void* table = nullptr;
+  const hipError_t err = scratch_address(&table);
+  if (err != hipSuccess) return err;
+  return launch_moe_route(indices, T, topk, E, offsets, row_token, row_of, table, stream);
 }
 
 // ----------------------------------------------------------------------------

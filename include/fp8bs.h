@@ -260,6 +260,22 @@ int fp8bs_moe_route(const int32_t* indices, int64_t T, int64_t topk, int64_t E, 
                     int64_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_noalloc -- fp8bs_moe_route with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The count table
+ * lives in a 1 MiB device array inside the library (one per GPU, held until
+ * the process ends); the call allocates nothing.  Limit:
+ * fp8bs_moe_route_workspace_size(T, topk, E) <= 1048576 bytes, i.e.
+ * ceil(T*topk/512) * E <= 262144 (e.g. 4096 tokens x top-8 with up to 4096
+ * experts), else FP8BS_ERR_SHAPE.  Every call on one GPU uses the same
+ * table: calls that overlap in time on one GPU (on different streams, or
+ * from several host threads without ordering) race and give wrong results.
+ * Other arguments, results and errors as fp8bs_moe_route.
+ */
+int fp8bs_moe_route_noalloc(const int32_t* indices, int64_t T, int64_t topk, int64_t E,
+                            int32_t* offsets, int32_t* row_token, int32_t* row_of, void* stream);
+
+/*
  * moe_quant_scatter -- the expert inputs: act_quant (as fp8bs_act_quant) of
  * every token row of x, written to each row its (token, slot) pairs were
  * routed to.  Quantisation is row local, so row r holds act_quant of

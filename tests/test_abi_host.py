@@ -100,6 +100,18 @@ def test_act_quant_launch_limits(L):
     assert g(P0, P1, P2, P3, lim // 2 + 1, 8, 64, 256, 0, None) == SHAPE
 
 
+def test_route_noalloc_validation(L):
+    """The workspace-free route: its table limit (1 MiB, i.e. ceil(T*topk/512)
+    * E <= 262144) and the usual checks, all before any HIP call."""
+    f = L.fp8bs_moe_route_noalloc
+    assert f(P0, 1 << 15, 8, 1024, P1, P2, P3, None) == SHAPE      # 512 x 1024 entries
+    assert f(P0, 1 << 14, 8, 1025, P1, P2, P3, None) == SHAPE      # 256 x 1025 entries
+    assert f(None, 1 << 14, 8, 1024, None, None, None, None) == NULL  # 256 x 1024: fits
+    assert f(P0, 4, 2, -1, P1, P2, P3, None) == SHAPE
+    assert f(P0, 4, 2, 8, P1 + 2, P2, P3, None) == ALIGN
+    assert f(P0, 4, 2, 8, P1, P1, P3, None) == ALIAS
+
+
 def test_weight_dequant_launch_limits(L):
     """One launch covers at most 2^32 - 1 threads: N*K + 255 < 2^32 for
     K % 16 != 0, ceil(N/4) * ceil(K/1024) < 2^24 workgroups for K % 16 == 0.
