@@ -18,8 +18,11 @@ milliseconds to settle (a GEMM's duration drifts by ~25% over its first
 ~30 ms), and the timed region is meant to see the steady state.  Kernel durations come from HIP
 events recorded on the stream the kernels run on; HBM-bound rows cycle through
 enough copies of their inputs that the 256 MB Infinity Cache cannot hold them.
+Secondary rows are timed as one replay of a HIP graph holding K back-to-back
+launches, so short kernels are not paced by the host's per-launch cost.
 The CPU baseline is the oracle (binary64 C + OpenMP) on a bounded sample of
-the same workload, timed on the host cores.
+the same workload, timed on the host cores, plus the oracle's wall time on
+each other hot-path row's shape (`per_op`), with the CPU model recorded.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -102,12 +105,28 @@ def warm(launch, copies, warmup):
     torch.cuda.synchronize()
 
 
-def timed(launch, copies, steps, warmup):
-    """Average duration (us) of `launch(i)`: one event pair brackets the whole
-    timed region of back-to-back launches on the launch stream, so per-launch
-    event overhead does not inflate short kernels."""
+def timed(launch, copies, steps, warmup, graph=True):
+    """Average duration (us) of `launch(i)` over `steps` back-to-back launches
+    on one stream, bracketed by one event pair.  With graph=True (the
+    secondary rows) the launches are first captured into a HIP graph and the
+    timed region is one replay of it, so the host's per-launch cost (Python
+    and ctypes, several us) does not pace short kernels; the headline GEMM is
+    timed with plain launches."""
     warm(launch, copies, warmup)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                launch(i % copies)
+        g.replay()                                 # first replay uploads the graph
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        del g
+        return start.elapsed_time(end) * 1e3 / steps
     start.record()
     for i in range(steps):
         launch(i % copies)
@@ -166,9 +185,29 @@ def bench_linear_step(M, N, K, cfg, steps, warmup, dev, fmt="fp32"):
         step()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    aq = timed(lambda c: fp8bs.fp8bs_act_quant(x, xq, xs, fmt), 1, steps, warmup)
-    gm = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, q, s, y), 1, steps, warmup)
+    aq = timed(lambda c: fp8bs.fp8bs_act_quant(x, xq, xs, fmt), 1, steps, warmup, graph=False)
+    gm = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, q, s, y), 1, steps, warmup, graph=False)
     return wall_ms, aq, gm, (x, q, s)
+
+
+def bench_linear_step_rotated(M, N, K, cfg, steps, warmup, dev):
+    """The headline step with x and W cycled over enough copies that the
+    Infinity Cache cannot hold them (the headline step reuses one x and one
+    W, which stay cache-resident); graph-replayed."""
+    copies = n_copies(2 * M * K + N * K)
+    xs = [inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 0) + 100 * c, dev)
+          for c in range(copies)]
+    ws = [quantised_weight(N, K, inputs.seed_for(cfg, 1) + 100 * c, dev) for c in range(copies)]
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    xsc = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step(c):
+        fp8bs.fp8bs_act_quant(xs[c], xq, xsc, "fp32")
+        fp8bs.fp8bs_gemm(xq, xsc, ws[c][0], ws[c][1], y)
+    us = timed(step, copies, steps, warmup)
+    del xs, ws
+    return us, copies
 
 
 def bench_decode(steps, warmup, dev, out):
@@ -392,12 +431,80 @@ def bench_mla(steps, warmup, dev, out):
             del sets, y
 
 
-def cpu_baseline(x_dev, w_dev, budget_s):
-    """The oracle on a row sample of the prefill linear: act_quant of the
-    sampled rows of x, then all N outputs of each sampled row in binary64, with
-    W quantised by the oracle itself from the same bf16 draw."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x_dev, w_dev, budget_s, dev):
+    """The oracle (binary64 C + OpenMP over all host threads) timed on the
+    host cores.  Headline `value`: act_quant of a row sample of the prefill
+    linear's x, then all N outputs of each sampled row, W quantised by the
+    oracle itself from the same bf16 draw.  `per_op`: wall time of the
+    oracle on each other hot-path row's workload shape (whole, or the sample
+    stated), with seeded inputs of the same shapes and distributions."""
     import oracle
     oracle.build()
+    per_op = {}
+
+    def clock(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def op(name, dt, work, unit, sample):
+        per_op[name] = {"ms": round(dt * 1e3, 2), unit: round(work / dt / 1e9, 3), "sample": sample}
+        log(f"  cpu {name:28s} {per_op[name]}")
+
+    # act_quant, both formats (full tensors)
+    for (M, K, fmt, cfg) in [(4096, 7168, oracle.FMT_FP32, 3), (1024, 7168, oracle.FMT_UE8M0, 5),
+                             (32, 7168, oracle.FMT_FP32, 2)]:
+        xb = inputs.bf16_bits(inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 50), dev).cpu())
+        dt = clock(lambda: oracle.act_quant(xb, fmt))
+        op(f"act_quant_{M}x{K}_{'ue8m0' if fmt else 'fp32'}", dt, act_quant_bytes(M, K), "gbs", "whole")
+    # weight_dequant [18432, 7168] (whole)
+    wq, ws = quantised_weight(18432, 7168, inputs.seed_for(5, 1), dev)
+    q, sc = wq.view(torch.uint8).cpu().numpy(), ws.cpu().numpy()
+    del wq, ws
+    dt = clock(lambda: oracle.weight_dequant(q, sc))
+    op("weight_dequant_18432x7168", dt, dequant_bytes(18432, 7168), "gbs", "whole")
+    del q, sc
+    # decode GEMM and the two GEMMs of the ue8m0 workload (whole)
+    for (M, N, K, fmt) in [(32, 18432, 7168, oracle.FMT_FP32), (1024, 1536, 7168, oracle.FMT_UE8M0),
+                           (1024, 16384, 512, oracle.FMT_UE8M0)]:
+        xb = inputs.bf16_bits(inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(5, 2), dev).cpu())
+        wb = inputs.bf16_bits(inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(5, 3), dev).cpu())
+        a, a_s = oracle.act_quant(xb, fmt)
+        b, b_s = oracle.weight_quant(wb)
+        dt = clock(lambda: oracle.gemm(a, a_s, b, b_s))
+        op(f"gemm_{M}x{N}x{K}", dt, 2 * M * N * K, "gflops", "whole")
+    # grouped MoE up projection on 16 of the 256 experts: every 16th in
+    # order of row count, so the sample spans the Zipf distribution
+    cfg = inputs.CONFIGS[4]
+    E, T, topk, N, K = cfg["experts"], cfg["tokens"], cfg["topk"], cfg["up"]["N"], cfg["up"]["K"]
+    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    counts = np.diff(route["offsets"])
+    pick = np.sort(np.argsort(counts, kind="stable")[::16])
+    rows = int(counts[pick].sum())
+    xb = inputs.bf16_bits(inputs.normal_bf16_device((rows, K), 1.0, inputs.seed_for(4, 0), dev).cpu())
+    a, a_s = oracle.act_quant(xb, oracle.FMT_FP32)
+    wb = inputs.bf16_bits(inputs.normal_bf16_device((len(pick) * N, K), 0.02, inputs.seed_for(4, 2),
+                                                    dev).cpu())
+    b, b_s = oracle.weight_quant(wb)
+    off = np.concatenate([[0], np.cumsum(counts[pick])]).astype(np.int32)
+    dt = clock(lambda: oracle.moe_gemm(a, a_s, b.reshape(len(pick), N, K),
+                                       b_s.reshape(len(pick), N // 128, K // 128), off))
+    op("moe_up_16_of_256_experts", dt, 2 * rows * N * K, "gflops",
+       f"every 16th expert by row count of the Zipf routing ({rows} of {T * topk} rows)")
+    del a, b, wb, xb
+
+    # headline: the prefill linear on a row sample
     M, K = x_dev.shape
     N = w_dev.shape[0]
     b, b_s = oracle.weight_quant(inputs.bf16_bits(w_dev.cpu()))
@@ -414,9 +521,10 @@ def cpu_baseline(x_dev, w_dev, budget_s):
     dt = run(rows)
     flops = 2 * rows * N * K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"act_quant + binary64 block-scaled GEMM of the first {rows} of the {M} rows "
-                      f"of the prefill linear (all {N} outputs per row, K={K}); {dt:.1f} s"}
+                      f"of the prefill linear (all {N} outputs per row, K={K}); {dt:.1f} s",
+            "per_op": per_op}
 
 
 def main():
@@ -427,7 +535,7 @@ def main():
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
                     "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,mla,down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (known traffic) so hardware byte "
                          "counters collected over this run can be scaled against it")
@@ -463,7 +571,7 @@ def main():
     rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
                                                          gemm_bytes(M, N, K), "mfma")
     sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "w8a16", "ue8m0",
-             "mla", "down"]) if args.rows == "all" else (
+             "mla", "down", "rotated"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
@@ -471,6 +579,11 @@ def main():
         rows["prefill_down_gemm_4096x7168x18432"] = row_result(
             "prefill down gemm", g2, 2 * d["M"] * d["N"] * d["K"], gemm_bytes(d["M"], d["N"], d["K"]),
             "mfma")
+    if "rotated" in sel:
+        r_us, r_copies = bench_linear_step_rotated(M, N, K, 3, args.steps, args.warmup, dev)
+        rows["prefill_linear_step_rotated"] = row_result(
+            "prefill step, rotated", r_us, flops, act_quant_bytes(M, K) + gemm_bytes(M, N, K), "mfma",
+            {"copies": r_copies})
     if "decode" in sel:
         bench_decode(args.steps, args.warmup, dev, rows)
     if "act_quant" in sel:
@@ -526,7 +639,7 @@ def main():
         log(f"cpu baseline: oracle on a row sample (~{args.cpu_seconds:.0f} s)")
         px, _, _ = prefill_inputs
         w_bf16 = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(3, 1), dev)
-        result["cpu_baseline"] = cpu_baseline(px, w_bf16, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(px, w_bf16, args.cpu_seconds, dev)
     print(json.dumps(result), flush=True)
 
 
