@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
     L.fp8bs_status_string.restype = ctypes.c_char_p
     L.fp8bs_version.restype = I
     L.fp8bs_act_quant.argtypes = [P, P, P, I64, I64, I, P]
+    L.fp8bs_e4m3_encode.argtypes = [P, P, I64, P]
     L.fp8bs_weight_quant.argtypes = [P, P, P, I64, I64, P]
     L.fp8bs_weight_dequant.argtypes = [P, P, P, I64, I64, P]
     L.fp8bs_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
@@ -232,6 +233,15 @@ def fp8bs_moe_route(indices: torch.Tensor, E: int, offsets: torch.Tensor, row_to
     _call("fp8bs_moe_route", _need(indices, (torch.int32,), "indices"), T, topk, E,
           _need(offsets, (torch.int32,), "offsets"), _need(row_token, (torch.int32,), "row_token"),
           _need(row_of, (torch.int32,), "row_of"), ws, nbytes, _stream(indices))
+
+
+def fp8bs_e4m3_encode(x: torch.Tensor, q: torch.Tensor) -> None:
+    """The float32 -> e4m3 conversion act_quant uses (RNE, saturating at 448):
+    q e4m3 [n] from x float32 [n]."""
+    if x.numel() != q.numel():
+        raise ValueError("x and q need the same number of elements")
+    _call("fp8bs_e4m3_encode", _need(x, (torch.float32,), "x"), _need(q, _F8, "q"),
+          x.numel(), _stream(x))
 
 
 def fp8bs_moe_route_noalloc(indices: torch.Tensor, E: int, offsets: torch.Tensor,

@@ -71,6 +71,15 @@ int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64
                                            scale_fmt == FP8BS_SCALE_UE8M0, (hipStream_t)stream));
 }
 
+int fp8bs_e4m3_encode(const float* x, void* q_e4m3, int64_t n, void* stream) {
+  if (n < 0 || !fp8bs::e4m3_encode_fits(n)) return FP8BS_ERR_SHAPE;
+  if (n == 0) return FP8BS_OK;
+  if (!x || !q_e4m3) return FP8BS_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q_e4m3, 4)) return FP8BS_ERR_ALIGN;
+  if (overlap(q_e4m3, n, x, 4 * n)) return FP8BS_ERR_ALIAS;
+  return status_of(fp8bs::launch_e4m3_encode(x, q_e4m3, n, (hipStream_t)stream));
+}
+
 static int weight_quant_entry(bool ue8m0, const void* w_bf16, void* q_e4m3, float* s, int64_t N,
                               int64_t K, void* stream) {
   if (N < 0 || K < 0) return FP8BS_ERR_SHAPE;

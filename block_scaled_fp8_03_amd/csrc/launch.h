@@ -13,6 +13,9 @@ namespace fp8bs {
 bool act_quant_fits(int64_t rows, int64_t K);
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
                             hipStream_t stream);
+// The float32 -> e4m3 conversion of act_quant / weight_quant on its own.
+bool e4m3_encode_fits(int64_t n);
+hipError_t launch_e4m3_encode(const float* x, void* q, int64_t n, hipStream_t stream);
 hipError_t launch_weight_quant(const void* w, void* q, float* s, int64_t N, int64_t K, bool ue8m0,
                                hipStream_t stream);
 // Whether one weight_dequant launch covers [N, K] (its grid's thread limit).

@@ -19,48 +19,56 @@ namespace fp8bs {
 // The input is a flat sequence of 128-element blocks (K % 128 == 0, row-major),
 // and block b's scale lives at s[b] ([M, K/128] row-major is that order).
 // A 16-lane row handles one block: lane i holds elements 8i .. 8i+7 (16 bytes
-// of bf16) and writes their 8 e4m3 bytes.  A 256-thread workgroup covers 16
-// blocks per pass and kAqPasses = 2 passes, all loads issued before any use.
-// With the non-temporal loads and stores this shape measured best against
-// 512 x 2, 1024 x 2, 512 x 4, 256 x 4 and 512 x 1 on every workload (same box:
-// 4096 x 18432 39.4 -> 38.3 us, 32768 x 2048 35.0 -> 34.1 us, 1024 x 7168 ue8m0
-// 6.5 -> 6.0 us, 4096 x 7168 cache-resident 16.3 -> 15.8 us, against 512 x 2).
+// of bf16) and writes their 8 e4m3 bytes.  A workgroup of THREADS threads
+// covers THREADS / 16 blocks per pass and PASSES passes, all loads issued
+// before any use.  Two launch shapes, by size (graph-replayed back-to-back
+// launches over inputs rotated past the Infinity Cache, same box, us):
+//   256 threads x 2 passes: 1024 x 7168 ue8m0 5.87, 32 x 7168 2.13 -- best
+//     on the small launches (a device copy of the same bytes: 6.34, 2.05);
+//   64 threads x 4 passes: 4096 x 7168 17.9 (256 x 2: 19.7), 4096 x 18432
+//     38.0 (42.3), 32768 x 2048 34.3 (37.2) -- best on the streaming ones
+//     (128 x 4, 256 x 4 within 2%; 256 x 1 and 128 x 2 slower).
+// Inputs of at least kAqLargeElems elements take the second shape.
 constexpr int kAqThreads = 256;
 constexpr int kAqPasses = 2;
 constexpr int kAqBlocksPerWg = (kAqThreads / 16) * kAqPasses;
+constexpr int kAqLargeThreads = 64;
+constexpr int kAqLargePasses = 4;
+constexpr int64_t kAqLargeElems = (int64_t)16 << 20;
 
 // SCATTER: x is the token matrix [T, K] and the codes and scale of token t's
 // block j go to every row r = row_of[t * topk + k] (k < topk, 0 <= r < R) of
 // q [R, K] / s [R, K/128] instead of to row t -- the expert inputs of the MoE
 // dispatch (quantisation is row local, so this equals quantising the
 // gathered rows).
-template <bool UE8M0, bool SCATTER>
-__global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __restrict__ x,
+template <bool UE8M0, bool SCATTER, int THREADS, int PASSES>
+__global__ __launch_bounds__(THREADS) void act_quant_kernel(const uint4* __restrict__ x,
                                                                uint2* __restrict__ q,
                                                                float* __restrict__ s,
                                                                int64_t nblocks,
                                                                const int32_t* __restrict__ row_of,
                                                                int topk, int64_t nb, int64_t R) {
+  constexpr int BPW = (THREADS / 16) * PASSES;             // blocks per workgroup
   const int lane16 = threadIdx.x & 15;
   const int row = threadIdx.x >> 4;
-  const int64_t wg_first = (int64_t)blockIdx.x * kAqBlocksPerWg;
+  const int64_t wg_first = (int64_t)blockIdx.x * BPW;
   const int64_t first = wg_first + row;
   // Loads through a buffer resource over this workgroup's blocks: blocks past
   // the end read zeros without a branch, so all passes' loads are in flight
   // together (bounds checks under branches had made the compiler wait for the
   // first two before issuing the rest).
-  const int64_t wg_blocks = min<int64_t>(nblocks - wg_first, kAqBlocksPerWg);
+  const int64_t wg_blocks = min<int64_t>(nblocks - wg_first, BPW);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint4*>(x + wg_first * 16), (short)0, (int)(uint32_t)(wg_blocks * 256), 0x00020000);
-  uint4 v[kAqPasses];
+  uint4 v[PASSES];
 #pragma unroll
-  for (int u = 0; u < kAqPasses; ++u) {
-    const uint32_t off = (uint32_t)(((row + u * (kAqThreads / 16)) * 16 + lane16) * 16);
+  for (int u = 0; u < PASSES; ++u) {
+    const uint32_t off = (uint32_t)(((row + u * (THREADS / 16)) * 16 + lane16) * 16);
     v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kNonTemporal));
   }
 #pragma unroll
-  for (int u = 0; u < kAqPasses; ++u) {
-    const int64_t b = first + u * (kAqThreads / 16);
+  for (int u = 0; u < PASSES; ++u) {
+    const int64_t b = first + u * (THREADS / 16);
     const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
     float f[8];
 #pragma unroll
@@ -103,8 +111,9 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(const uint4* __re
   }
 }
 
-// The grid is one-dimensional, ceil(nblocks / kAqBlocksPerWg) workgroups of
-// kAqThreads threads: at most 2^32 - 1 threads per launch.
+// The grid is one-dimensional: at most 2^32 - 1 threads per launch.  The
+// 256 x 2 shape takes the most threads per block (8), so its limit,
+// nblocks <= floor((2^32 - 1) / 256) * 32, holds for both shapes.
 bool act_quant_fits(int64_t rows, int64_t K) {
   if (rows <= 0 || K <= 0) return true;
   const int64_t max_wg = (((int64_t)1 << 32) - 1) / kAqThreads;
@@ -112,18 +121,31 @@ bool act_quant_fits(int64_t rows, int64_t K) {
   return rows <= max_wg * kAqBlocksPerWg / nb;
 }
 
+// One launch of the kernel for nblocks blocks of x (T token rows for SCATTER).
+template <bool UE8M0, bool SCATTER>
+void launch_aq(const void* x, void* q, float* s, int64_t nblocks, const int32_t* row_of, int topk,
+               int64_t nb, int64_t R, hipStream_t stream) {
+  if (nblocks * kBlock >= kAqLargeElems) {
+    constexpr int BPW = (kAqLargeThreads / 16) * kAqLargePasses;
+    const int64_t grid = (nblocks + BPW - 1) / BPW;
+    act_quant_kernel<UE8M0, SCATTER, kAqLargeThreads, kAqLargePasses>
+        <<<dim3((unsigned)grid), dim3(kAqLargeThreads), 0, stream>>>((const uint4*)x, (uint2*)q, s, nblocks,
+                                                                     row_of, topk, nb, R);
+  } else {
+    const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
+    act_quant_kernel<UE8M0, SCATTER, kAqThreads, kAqPasses>
+        <<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>((const uint4*)x, (uint2*)q, s, nblocks,
+                                                                row_of, topk, nb, R);
+  }
+}
+
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K, bool ue8m0,
                             hipStream_t stream) {
   const int64_t nblocks = M * (K / kBlock);
   if (nblocks == 0) return hipSuccess;
   if (!act_quant_fits(M, K)) return hipErrorInvalidConfiguration;
-  const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
-  if (ue8m0)
-    act_quant_kernel<true, false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
-        (const uint4*)x, (uint2*)q, s, nblocks, nullptr, 0, 0, 0);
-  else
-    act_quant_kernel<false, false><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
-        (const uint4*)x, (uint2*)q, s, nblocks, nullptr, 0, 0, 0);
+  if (ue8m0) launch_aq<true, false>(x, q, s, nblocks, nullptr, 0, 0, 0, stream);
+  else launch_aq<false, false>(x, q, s, nblocks, nullptr, 0, 0, 0, stream);
   return hipGetLastError();
 }
 
@@ -134,13 +156,38 @@ hipError_t launch_moe_quant_scatter(const void* x, const int32_t* row_of, void* 
   const int64_t nblocks = T * nb;
   if (nblocks == 0 || R == 0) return hipSuccess;
   if (!act_quant_fits(T, K)) return hipErrorInvalidConfiguration;
-  const int64_t grid = (nblocks + kAqBlocksPerWg - 1) / kAqBlocksPerWg;
-  if (ue8m0)
-    act_quant_kernel<true, true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
-        (const uint4*)x, (uint2*)q, s, nblocks, row_of, (int)topk, nb, R);
-  else
-    act_quant_kernel<false, true><<<dim3((unsigned)grid), dim3(kAqThreads), 0, stream>>>(
-        (const uint4*)x, (uint2*)q, s, nblocks, row_of, (int)topk, nb, R);
+  if (ue8m0) launch_aq<true, true>(x, q, s, nblocks, row_of, (int)topk, nb, R, stream);
+  else launch_aq<false, true>(x, q, s, nblocks, row_of, (int)topk, nb, R, stream);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// e4m3_encode: the float32 -> e4m3 step of act_quant and weight_quant alone
+// ----------------------------------------------------------------------------
+// q[i] = pack4_e4m3's encoding of x[i]: clamp to [-448, 448], then the
+// hardware conversion (round to nearest, ties to even).  Thread t encodes
+// x[4t .. 4t+3] with one 16-byte load and one 4-byte store; a partial last
+// group goes element by element.
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ x,
+                                                          uint8_t* __restrict__ q, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 v = *(const float4*)(x + i);
+    *(uint32_t*)(q + i) = pack4_e4m3(v.x, v.y, v.z, v.w);
+  } else if (i < n) {
+    for (int64_t k = i; k < n; ++k) q[k] = (uint8_t)(pack4_e4m3(x[k], 0.0f, 0.0f, 0.0f) & 0xFFu);
+  }
+}
+
+bool e4m3_encode_fits(int64_t n) {
+  return n <= ((((int64_t)1 << 32) - 1) / 256) * 256 * 4;
+}
+
+hipError_t launch_e4m3_encode(const float* x, void* q, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  if (!e4m3_encode_fits(n)) return hipErrorInvalidConfiguration;
+  const int64_t grid = (n + 1023) / 1024;
+  e4m3_encode_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(x, (uint8_t*)q, n);
   return hipGetLastError();
 }
 

@@ -86,6 +86,22 @@ int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64
                     int scale_fmt, void* stream);
 
 /*
+ * e4m3_encode -- the float32 -> e4m3 step of act_quant and weight_quant on
+ * its own (the cast to float8_e4m3fn of Admin guide 8.5.1): q[i] is x[i]
+ * rounded to the nearest e4m3 value, ties to even mantissa, magnitudes
+ * above 448 saturating to +-448 (464, the midpoint to the next binade,
+ * rounds to 448); the sign of a zero result follows x.  Exposed so that
+ * the hardware conversion can be checked against a reference over every
+ * float32 input.
+ *
+ *   x       in   float32 [n] (16-byte aligned)
+ *   q_e4m3  out  e4m3 [n] (4-byte aligned, must not overlap x)
+ *   n >= 0; n <= 2^34 - 1024 (one launch), else FP8BS_ERR_SHAPE.
+ *   NaN inputs are outside the contract.
+ */
+int fp8bs_e4m3_encode(const float* x, void* q_e4m3, int64_t n, void* stream);
+
+/*
  * weight_quant -- 128x128-block weight quantisation with the same rule as
  * act_quant (fp32 scale format).  The pages ship weights already quantised
  * (Admin guide 6.3: one float32 scale per 128 x 128 block, shape

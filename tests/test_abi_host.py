@@ -83,6 +83,19 @@ def test_weight_quant_and_dequant_validation(L):
     assert L.fp8bs_weight_dequant(None, None, None, 7, 0, None) == OK
 
 
+def test_e4m3_encode_validation(L):
+    f = L.fp8bs_e4m3_encode
+    assert f(P0, P1, -1, None) == SHAPE
+    assert f(None, None, 0, None) == OK
+    assert f(None, P1, 8, None) == NULL
+    assert f(P0 + 4, P1, 8, None) == ALIGN
+    assert f(P0, P1 + 2, 8, None) == ALIGN
+    assert f(P0, P0 + 16, 8, None) == ALIAS
+    lim = ((2 ** 32 - 1) // 256) * 1024
+    assert f(None, None, lim, None) == NULL
+    assert f(P0, P1, lim + 1, None) == SHAPE
+
+
 def test_act_quant_launch_limits(L):
     """One act_quant launch covers at most 2^32 - 1 threads: 256-thread
     workgroups of 32 blocks, so M * (K / 128) <= 16777215 * 32 = 536870880

@@ -141,3 +141,34 @@ def test_weight_dequant_full_size():
     w = inputs.normal_bf16((18432, 7168), 0.02, inputs.seed_for(5, 1))
     q, s = oracle.weight_quant(inputs.bf16_bits(w))
     check_dequant(q, s, "weight_dequant[18432x7168]")
+
+
+def test_e4m3_encoder_exhaustive():
+    """The hardware float32 -> e4m3 conversion used by act_quant and
+    weight_quant (clamp to +-448, then round to nearest even), checked
+    against the oracle's encoder on every float32 bit pattern of magnitude
+    <= 464 (the midpoint above 448), both signs: about 2.3e9 values, in
+    chunks of 2^28 generated on the device from their bit patterns."""
+    top = int(np.float32(464.0).view(np.uint32))             # 0x43E80000
+    chunk = 1 << 28
+    x = torch.empty(chunk, dtype=torch.float32, device=DEV)
+    q = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    checked = 0
+    for sign in (0, 0x80000000):
+        for lo in range(0, top + 1, chunk):
+            n = min(chunk, top + 1 - lo)
+            bits = torch.arange(lo, lo + n, dtype=torch.int64, device=DEV) | sign
+            x[:n] = bits.to(torch.int32).view(torch.float32) if sign == 0 else \
+                (bits - (1 << 32)).to(torch.int32).view(torch.float32)
+            del bits
+            fp8bs.fp8bs_e4m3_encode(x[:n], q[:n])
+            got = q[:n].cpu().numpy()
+            ref_in = (np.arange(lo, lo + n, dtype=np.uint64) | sign).astype(np.uint32).view(np.float32)
+            ref = oracle.e4m3_encode_f32(ref_in)
+            if not np.array_equal(got, ref):
+                bad = np.nonzero(got != ref)[0][:8]
+                raise AssertionError(f"e4m3 encode differs at bit patterns "
+                                     f"{[hex(int(ref_in[i].view(np.uint32))) for i in bad]}: gpu "
+                                     f"{[hex(int(got[i])) for i in bad]} oracle {[hex(int(ref[i])) for i in bad]}")
+            checked += n
+    assert checked == 2 * (top + 1)
