@@ -363,12 +363,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
   for (int s = 0; s < ST - 1; ++s)
     if (s < nkb) issue(s, s);
 
+  // The fold of a K block's last row block is deferred to just after the
+  // next barrier: its MFMAs then run on through the barrier wait instead of
+  // draining the matrix pipe before it.
+  v4f pend[NT];
+  float pend_sc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) pend[j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   for (int kb = 0; kb < nkb; ++kb) {
     const int st = kb % ST;
     // DMA for kb is complete once at most the later stages' ops are pending.
     if (kb + ST - 2 < nkb) wait_vmcnt<(ST - 2) * LPS>();
     else wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
     barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
 
     const uint8_t* sbase = smem + st * STAGE;
     // fragment rows 16 i .. 16 i + 15 from the lane bases (lo, hi)
@@ -394,6 +403,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
     // DMA instructions.  It fills the other stage (and possibly the other a_s
     // chunk buffer), which every wave finished reading before the barrier.
     if (kb + ST - 1 < nkb) issue(kb + ST - 1, (kb + ST - 1) % ST);
+    if (!E8) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        acc[j][MT - 1][0] = __builtin_fmaf(pend[j][0], pend_sc, acc[j][MT - 1][0]);
+        acc[j][MT - 1][1] = __builtin_fmaf(pend[j][1], pend_sc, acc[j][MT - 1][1]);
+        acc[j][MT - 1][2] = __builtin_fmaf(pend[j][2], pend_sc, acc[j][MT - 1][2]);
+        acc[j][MT - 1][3] = __builtin_fmaf(pend[j][3], pend_sc, acc[j][MT - 1][3]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const v8i af = t == 0 ? af0 : frag(a_lo, a_hi, t);
@@ -408,6 +426,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         continue;
       }
       const float sc = as_t * bsv;
+      if (t == MT - 1) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) pend[j] = mfma_k128(bf[j], af);
+        pend_sc = sc;
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const v4f pr = mfma_k128(bf[j], af);
@@ -416,6 +440,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, in
         acc[j][t][2] = __builtin_fmaf(pr[2], sc, acc[j][t][2]);
         acc[j][t][3] = __builtin_fmaf(pr[3], sc, acc[j][t][3]);
       }
+    }
+  }
+  if (!E8) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      acc[j][MT - 1][0] = __builtin_fmaf(pend[j][0], pend_sc, acc[j][MT - 1][0]);
+      acc[j][MT - 1][1] = __builtin_fmaf(pend[j][1], pend_sc, acc[j][MT - 1][1]);
+      acc[j][MT - 1][2] = __builtin_fmaf(pend[j][2], pend_sc, acc[j][MT - 1][2]);
+      acc[j][MT - 1][3] = __builtin_fmaf(pend[j][3], pend_sc, acc[j][MT - 1][3]);
     }
   }
 
