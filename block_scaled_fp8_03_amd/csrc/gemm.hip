@@ -1543,8 +1543,10 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   constexpr int BM = 256, BN = 256;
   // Smaller GEMMs whose 256 x 256 tiles cannot fill the CUs run on 128 x 128
   // tiles when those give at least one tile per two CUs, else on 64 x 64
-  // tiles with two workgroups per CU (measured: 1024 x 1536 x 7168 104 ->
-  // 30 us; 1024 x 3072 x 7168 104 -> 47 us).
+  // tiles with four LDS stages, two workgroups per CU (measured: 1024 x 1536
+  // x 7168 104 -> 30 us against one 256 x 256 tile per CU, then 30.2 -> 27.9
+  // us with four stages instead of three; these tiles are bound by operand
+  // fetch, 17 KB per 1 MFLOP K block).
   const int cus = device_cus();
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(BM, BN) < cus) {
@@ -1555,7 +1557,7 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
     }
     p.num_m = (int)((M + 63) / 64);
     p.num_n = (int)((N + 63) / 64);
-    return run_tile<64, 64, 32, 32, 3, 4, 2, 2, E8>(p, out_f32, p.num_m * p.num_n, stream);
+    return run_tile<64, 64, 32, 32, 4, 4, 2, 2, E8>(p, out_f32, p.num_m * p.num_n, stream);
   }
   p.num_m = (int)((M + BM - 1) / BM);
   p.num_n = (int)((N + BN - 1) / BN);
