@@ -249,6 +249,16 @@ def bench_act_quant(steps, warmup, dev, out):
         out[f"act_quant_{M}x{K}_{fmt}"] = row_result(f"act_quant {M}x{K} {fmt}", us, None, nb, "hbm",
                                                      {"copies": copies})
         del xs_in, qs, ss
+        # reference: a plain device copy moving the same bytes (half read, half
+        # written), rotated and timed the same way -- what a streaming kernel of
+        # this size reaches on the box
+        half = nb // 2 // 16 * 16
+        srcs = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        us = timed(lambda c: dsts[c].copy_(srcs[c]), copies, steps, warmup)
+        out[f"copy_reference_{M}x{K}"] = row_result(f"device copy, bytes of {M}x{K}", us, None, 2 * half,
+                                                    "hbm", {"copies": copies})
+        del srcs, dsts
 
 
 def bench_dequant(steps, warmup, dev, out):
