@@ -904,15 +904,17 @@ gemm_decode8_kernel(GemmParams p, int rows) {
   constexpr int AS_BYTES = KPS * 256;                             // [row][4] or [4][row]
   constexpr int STAGE = B_BYTES + A_BYTES + AS_BYTES;
   constexpr int N_AS = CH ? 1 : KPS;
-  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP, N_REAL = N_B + N_A + N_AS;
-  constexpr int LPS = (N_REAL + NW - 1) / NW;
+  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP;
+  constexpr int IB = (N_B + NW - 1) / NW, IA = (N_A + NW - 1) / NW;  // load slots per wave
+  constexpr int LPS = IB + IA + 1;                                // + one for the activation scales
   constexpr int NTW = 3;                                          // tiles per wave (set 1: 2)
-  static_assert(N_REAL <= NW * LPS && MR <= 32, "shape");
-  static_assert(ST * STAGE + 256 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 256];
+  static_assert(N_A == NW * IA && N_AS <= NW && MR <= 32, "shape");
+  static_assert(ST * STAGE + 1024 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 1024];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);
   const int g = lane >> 4, r16 = lane & 15;
   const int M = p.rows, N = p.N, K = p.K;
   const int nkb = K / 128, nkc = (nkb + KPS - 1) / KPS;
@@ -931,54 +933,55 @@ gemm_decode8_kernel(GemmParams p, int rows) {
   const uint32_t smem_lds = lds_addr(smem);
   const uint32_t dummy_lds = smem_lds + ST * STAGE;
 
-  // DMA instruction u = wave + NW i of a stage (wave-uniform type):
-  //   u < N_B                weight rows: K block u / GRP, row group u % GRP
-  //   u < N_B + N_A          activations: K block v / AGRP, row group v % AGRP
-  //   u < N_B + N_A + N_AS   a_s: CH: lane = row, its 4 K blocks (16 bytes);
-  //                          else K block u - N_B - N_A, lane = activation row
-  //   otherwise              padding (out of range -> zeros into the dummy area)
-  // 16-byte loads: lane l takes row l / 8 of its group and logical chunk
-  // (l % 8) ^ (l / 8), the row's swizzle (row % 8 = l / 8).
+  // The LPS DMA instructions of a wave in a stage have a type fixed by their
+  // slot i, so the issue is straight-line code (a per-load type chosen at run
+  // time had compiled to a chain of scalar branches in front of every load,
+  // all on the path from the barrier to the next stage's requests):
+  //   i < IB        weight rows, u = wave + NW i < N_B: K block u / GRP, row
+  //                 group u % GRP (u >= N_B: padding);
+  //   i < IB + IA   activations, v = wave + NW (i - IB): K block v / AGRP,
+  //                 row group v % AGRP;
+  //   i = IB + IA   a_s: CH: wave 0, lane = row, its 4 K blocks (16 bytes);
+  //                 else waves 0 .. KPS - 1, K block `wave`, lane = row.
+  // Padding loads are out of range (zeros) into the 1 KB dummy area.  16-byte
+  // loads: lane l takes row l / 8 of its group and logical chunk
+  // (l % 8) ^ (l / 8), the row's swizzle (row % 8 = l / 8).  The stage's K
+  // position goes in the scalar offset field.
   const int lchunk = (lane & 7) ^ (lane >> 3);
-  uint32_t voff[LPS], lds_off[LPS], kstep[LPS];
+  uint32_t voff[LPS], lds_off[LPS];
+  bool real[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
-    const int u = wave + NW * i;
-    if (u < N_B) {
-      const int kq = u / GRP, grp = u % GRP;
-      voff[i] = 8 * grp < rows ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq
-                               : 0xF0000000u;
+    if (i < IB) {
+      const int u = wave + NW * i, kq = u / GRP, grp = u % GRP;
+      real[i] = u < N_B;
+      voff[i] = real[i] && 8 * grp < rows
+                    ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq
+                    : 0xF0000000u;
       lds_off[i] = kq * B_TILE + grp * 1024;
-      kstep[i] = KPS * 128;
-    } else if (u < N_B + N_A) {
-      const int v = u - N_B, kq = v / AGRP, grp = v % AGRP;
+    } else if (i < IB + IA) {
+      const int v = wave + NW * (i - IB), kq = v / AGRP, grp = v % AGRP;
+      real[i] = true;
       voff[i] = (uint32_t)(8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq;
       lds_off[i] = B_BYTES + kq * A_TILE + grp * 1024;
-      kstep[i] = KPS * 128;
-    } else if (u < N_B + N_A + N_AS) {
-      const int kq = CH ? 0 : u - N_B - N_A;
-      voff[i] = (uint32_t)lane * nkb * 4 + 4 * kq;
-      lds_off[i] = B_BYTES + A_BYTES + kq * 256;
-      kstep[i] = KPS * 4;
     } else {
-      voff[i] = 0xF0000000u;
-      lds_off[i] = 0;
-      kstep[i] = 0;
+      const int kq = CH ? 0 : wave;
+      real[i] = wave < N_AS;
+      voff[i] = real[i] ? (uint32_t)lane * nkb * 4 + 4 * kq : 0xF0000000u;
+      lds_off[i] = B_BYTES + A_BYTES + kq * 256;
     }
   }
 
   auto issue = [&](int kc, int st) {
     const uint32_t base = smem_lds + st * STAGE;
+    const uint32_t kofs = (uint32_t)kc * (KPS * 128), sofs = (uint32_t)kc * (KPS * 4);
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      const int u = wave + NW * i;                        // wave-uniform: scalar branches
-      const uint32_t off = voff[i] + (uint32_t)kc * kstep[i];
-      if (u < N_B) dma_b128_nt(b_rsrc, base + lds_off[i], off);
-      else if (u < N_B + N_A) dma_b128(a_rsrc, base + lds_off[i], off);
-      else if (u < N_B + N_A + N_AS) {
-        if (CH) dma_b128(as_rsrc, base + lds_off[i], off);
-        else dma_b32(as_rsrc, base + lds_off[i], off);
-      } else dma_b32(as_rsrc, dummy_lds, 0xF0000000u);
+      const uint32_t lds = real[i] ? base + lds_off[i] : dummy_lds;
+      if (i < IB) dma_b128s_nt(b_rsrc, lds, voff[i], kofs);
+      else if (i < IB + IA) dma_b128s(a_rsrc, lds, voff[i], kofs);
+      else if (CH) dma_b128s(as_rsrc, lds, voff[i], sofs);
+      else dma_b32s(as_rsrc, lds, voff[i], sofs);
     }
   };
 
@@ -1113,15 +1116,17 @@ w8a16_decode8_kernel(GemmParams p, int rows) {
   constexpr int B_TILE = kDecode8Rows * 128, A_TILE = MR * 256;   // one K block
   constexpr int B_BYTES = KPS * B_TILE, A_BYTES = KPS * A_TILE;
   constexpr int STAGE = B_BYTES + A_BYTES;
-  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP, N_REAL = N_B + N_A;
-  constexpr int LPS = (N_REAL + NW - 1) / NW;
+  constexpr int N_B = KPS * GRP, N_A = KPS * AGRP;
+  constexpr int IB = (N_B + NW - 1) / NW, IA = N_A / NW;          // load slots per wave
+  constexpr int LPS = IB + IA;
   constexpr int NTW = 2;                                          // tiles per wave (sets 1-3: 1)
-  static_assert(MR <= 32, "shape");
-  static_assert(ST * STAGE + 256 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 256];
+  static_assert(MR <= 32 && N_A == NW * IA, "shape");
+  static_assert(ST * STAGE + 1024 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE + 1024];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);
   const int g = lane >> 4, r16 = lane & 15;
   const int M = p.rows, N = p.N, K = p.K;
   const int nkb = K / 128, nkc = (nkb + KPS - 1) / KPS;
@@ -1140,46 +1145,45 @@ w8a16_decode8_kernel(GemmParams p, int rows) {
   const uint32_t smem_lds = lds_addr(smem);
   const uint32_t dummy_lds = smem_lds + ST * STAGE;
 
-  // DMA instruction u = wave + NW i of a stage:
-  //   u < N_B          weight rows: K block u / GRP, 8-row group u % GRP; lane l
-  //                    takes row l / 8, logical chunk (l % 8) ^ (l / 8)
-  //   u < N_B + N_A    x rows: K block v / AGRP, 4-row group v % AGRP; lane l
-  //                    takes row l / 16, logical chunk (l % 16) ^ swz256(row)
-  //   otherwise        padding (out of range -> zeros into the dummy area)
-  uint32_t voff[LPS], lds_off[LPS], kstep[LPS];
+  // The LPS DMA instructions of a wave in a stage have a type fixed by their
+  // slot i (straight-line issue, as in gemm_decode8_kernel):
+  //   i < IB   weight rows, u = wave + NW i < N_B: K block u / GRP, 8-row group
+  //            u % GRP; lane l takes row l / 8, logical chunk (l % 8) ^ (l / 8)
+  //            (u >= N_B: padding, out of range into the 1 KB dummy area);
+  //   else     x rows, v = wave + NW (i - IB): K block v / AGRP, 4-row group
+  //            v % AGRP; lane l takes row l / 16, logical chunk
+  //            (l % 16) ^ swz256(row).
+  // The stage's K position goes in the scalar offset field.
+  uint32_t voff[LPS], lds_off[LPS];
+  bool real[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
-    const int u = wave + NW * i;
-    if (u < N_B) {
-      const int kq = u / GRP, grp = u % GRP;
+    if (i < IB) {
+      const int u = wave + NW * i, kq = u / GRP, grp = u % GRP;
       const int lchunk = (lane & 7) ^ (lane >> 3);
-      voff[i] = 8 * grp < rows ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq
-                               : 0xF0000000u;
+      real[i] = u < N_B;
+      voff[i] = real[i] && 8 * grp < rows
+                    ? (uint32_t)(n_base + 8 * grp + (lane >> 3)) * K + 16 * lchunk + 128 * kq
+                    : 0xF0000000u;
       lds_off[i] = kq * B_TILE + grp * 1024;
-      kstep[i] = KPS * 128;
-    } else if (u < N_REAL) {
-      const int v = u - N_B, kq = v / AGRP, grp = v % AGRP;
+    } else {
+      const int v = wave + NW * (i - IB), kq = v / AGRP, grp = v % AGRP;
       const int r = 4 * grp + (lane >> 4);
       const int lchunk = (lane & 15) ^ swz256(r & 15);
+      real[i] = true;
       voff[i] = (uint32_t)r * (2 * K) + 16 * lchunk + 256 * kq;   // rows >= M read zeros
       lds_off[i] = B_BYTES + kq * A_TILE + grp * 1024;
-      kstep[i] = KPS * 256;
-    } else {
-      voff[i] = 0xF0000000u;
-      lds_off[i] = 0;
-      kstep[i] = 0;
     }
   }
 
   auto issue = [&](int kc, int st) {
     const uint32_t base = smem_lds + st * STAGE;
+    const uint32_t bofs = (uint32_t)kc * (KPS * 128), xofs = (uint32_t)kc * (KPS * 256);
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      const int u = wave + NW * i;                        // wave-uniform: scalar branches
-      const uint32_t off = voff[i] + (uint32_t)kc * kstep[i];
-      if (u < N_B) dma_b128_nt(b_rsrc, base + lds_off[i], off);
-      else if (u < N_REAL) dma_b128(a_rsrc, base + lds_off[i], off);
-      else dma_b32(a_rsrc, dummy_lds, 0xF0000000u);
+      const uint32_t lds = real[i] ? base + lds_off[i] : dummy_lds;
+      if (i < IB) dma_b128s_nt(b_rsrc, lds, voff[i], bofs);
+      else dma_b128s(a_rsrc, lds, voff[i], xofs);
     }
   };
 
