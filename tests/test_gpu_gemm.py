@@ -348,6 +348,7 @@ def _moe_operands_from_counts(counts, N, K, seed):
     ("large only", 5, 300, 128, 3),           # every expert > 64 rows, ragged N
     ("one row", 1, 256, 128, 4),
     ("few tiles", 9, 256, 128, 5),            # fewer tiles than XCDs in a class
+    ("m tile boundaries", 12, 384, 256, 6),   # large m tiles of 1, 128, 129 and 256 rows
 ])
 def test_moe_schedule(name, E, N, K, seed):
     """The one-launch schedule of both expert classes (tiles of each class
@@ -365,6 +366,10 @@ def test_moe_schedule(name, E, N, K, seed):
         counts = rng.integers(65, 700, E)
     elif name == "one row":
         counts = np.array([1])
+    elif name == "m tile boundaries":
+        # a large expert's m tile of at most 128 rows skips its empty half's
+        # MFMAs; these counts put its rows on both sides of 128 and 256
+        counts = np.array([65, 128, 129, 255, 256, 257, 384, 385, 512, 640, 3, 64])
     else:
         counts = np.array([0, 70, 3, 0, 0, 64, 65, 1, 0])
     a, a_s, b, b_s, off = _moe_operands_from_counts(counts.astype(np.int64), N, K, 7000 + seed)
