@@ -441,6 +441,39 @@ def bench_mla(steps, warmup, dev, out):
             del sets, y
 
 
+def bench_vendor(steps, warmup, dev, out):
+    """Context, not part of the path: the vendor library's plain FP8 GEMM
+    (hipBLASLt through torch._scaled_mm, one per-tensor scale, so no block
+    scales and no per-K-block fold) next to this library's GEMM with float32
+    block scales and with ue8m0 scales, on the same codes, timed the same way
+    (graph replays, no rotation), at the prefill up and down shapes and at
+    4096 x 16384 x 7168, whose 256 x 256 tiles fill whole rounds of the CUs."""
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    for (M, N, K) in [(4096, 18432, 7168), (4096, 7168, 18432), (4096, 16384, 7168)]:
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(3, 20), dev)
+        w = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(3, 21), dev)
+        xq, xs = fp8bs.act_quant(x)
+        xe, xse = fp8bs.act_quant(x, "ue8m0")
+        wq, ws = fp8bs.weight_quant(w)
+        we, wse = fp8bs.weight_quant(w, "ue8m0")
+        del x, w
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        flops = 2 * M * N * K
+        tag = f"{M}x{N}x{K}"
+        us = timed(lambda c: torch._scaled_mm(xq, wq.t(), scale_a=one, scale_b=one,
+                                              out_dtype=torch.bfloat16), 1, steps, warmup)
+        out[f"vendor_hipblaslt_plain_fp8_{tag}"] = row_result(
+            f"hipBLASLt plain fp8 {tag}", us, flops, None, "mfma",
+            {"note": "torch._scaled_mm, per-tensor scales: context, not this library"})
+        us = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, wq, ws, y), 1, steps, warmup)
+        out[f"vendor_cmp_fp8bs_fp32_scales_{tag}"] = row_result(f"fp8bs fp32 scales {tag}", us, flops,
+                                                                 None, "mfma")
+        us = timed(lambda c: fp8bs.fp8bs_gemm(xe, xse, we, wse, y, ue8m0=True), 1, steps, warmup)
+        out[f"vendor_cmp_fp8bs_ue8m0_{tag}"] = row_result(f"fp8bs ue8m0 {tag}", us, flops, None, "mfma")
+        del xq, xs, xe, xse, wq, ws, we, wse, y
+        torch.cuda.empty_cache()
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -543,7 +576,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
-                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,mla,down")
+                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,mla,down,rotated; "
+                    "'vendor' (not in all) adds the vendor library's plain FP8 GEMM for context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -612,6 +646,8 @@ def main():
         bench_ue8m0(args.steps, args.warmup, dev, rows)
     if "mla" in sel:
         bench_mla(args.steps, args.warmup, dev, rows)
+    if "vendor" in sel:
+        bench_vendor(args.steps, args.warmup, dev, rows)
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8bs.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "gemm.hip", "moe_dispatch.hip", "mla.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_e8.hip", "moe_dispatch.hip", "mla.hip", "abi.cpp"]
 
 COMMON_FLAGS = [
     "-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -30,15 +30,18 @@ COMMON_FLAGS = [
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the per-K-block scale fold reads them with VALU
-    # FMAs, which cannot take AGPR operands.
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+# MFMA results in VGPRs: the per-K-block scale fold reads them with VALU FMAs,
+# which cannot take AGPR operands.  gemm_e8.hip has no fold and keeps its 256
+# accumulators per lane in AGPRs, so it is built without this.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+AGPR_SOURCES = {"gemm_e8.hip"}
 
 
 def _compile(src: str, build_dir: str) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    form = [] if src in AGPR_SOURCES else VGPR_FORM
+    cmd = [HIPCC, *COMMON_FLAGS, *HIP_FLAGS, *form, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON_FLAGS, "--offload-arch=gfx950", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
