@@ -81,6 +81,8 @@ int fp8bs_version(void);
  *   M * (K / 128) <= 536870880 (M * K up to about 2^36); larger shapes
  *   return FP8BS_ERR_SHAPE.
  *   All three pointers 16-byte aligned except `s` (4-byte).
+ *   x must be finite: a block holding +-Inf or NaN gets an unspecified scale
+ *   and unspecified codes (the rule above is not defined for it).
  */
 int fp8bs_act_quant(const void* x_bf16, void* q_e4m3, float* s, int64_t M, int64_t K,
                     int scale_fmt, void* stream);
