@@ -576,8 +576,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rows", default="all", help="secondary rows: all, none, or a comma list of "
-                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,mla,down,rotated; "
-                    "'vendor' (not in all) adds the vendor library's plain FP8 GEMM for context")
+                    "decode,act_quant,dequant,small,moe,dispatch,w8a16,ue8m0,mla,down,rotated,vendor "
+                    "(vendor: the vendor library's plain FP8 GEMM next to this one's, for context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -615,7 +615,7 @@ def main():
     rows["prefill_up_gemm_4096x18432x7168"] = row_result("prefill gemm", gm_us, flops,
                                                          gemm_bytes(M, N, K), "mfma")
     sel = set(["decode", "act_quant", "dequant", "small", "moe", "dispatch", "w8a16", "ue8m0",
-             "mla", "down", "rotated"]) if args.rows == "all" else (
+             "mla", "down", "rotated", "vendor"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
@@ -647,7 +647,11 @@ def main():
     if "mla" in sel:
         bench_mla(args.steps, args.warmup, dev, rows)
     if "vendor" in sel:
-        bench_vendor(args.steps, args.warmup, dev, rows)
+        try:
+            bench_vendor(args.steps, args.warmup, dev, rows)
+        except Exception as e:                     # context only: never fail the run for it
+            rows["vendor_hipblaslt_plain_fp8"] = {"error": f"{type(e).__name__}: {e}"[:200]}
+            torch.cuda.empty_cache()
     torch.cuda.empty_cache()
 
     gemm_tflops = flops / gm_us / 1e6
