@@ -4,8 +4,9 @@
 // "DeepSeek-V3 User Guide" FAQ): each K block's 128-wide products are scaled
 // by the MFMA itself (v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0
 // exponents of the activation row and the weight block) and accumulated in
-// float32, K block after K block, so there is no VALU fold and the
-// accumulators need never leave the matrix unit's registers.
+// float32, K block after K block, so there is no VALU fold and no VALU
+// instruction ever reads the accumulators before the epilogue: they can live
+// in AGPRs, which VALU instructions cannot address.
 //
 // Layout.  A 256 x 256 tile of C per workgroup of four waves, one per SIMD;
 // wave (wm, wn) owns rows 128 wm .. +127 and columns 128 wn .. +127, i.e. 8 x
