@@ -166,12 +166,12 @@ def row_result(name, us, flops=None, nbytes=None, bound="hbm", extra=None):
     return r
 
 
-def bench_linear_step(M, N, K, cfg, steps, warmup, dev, fmt="fp32"):
+def bench_linear_step(M, N, K, sid, steps, warmup, dev, fmt="fp32"):
     """The FP8 linear (act_quant then GEMM) of one workload.  Returns the wall
     time per step over the timed region, and each kernel's average duration
     from its own back-to-back timed region."""
-    x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 0), dev)
-    q, s = quantised_weight(N, K, inputs.seed_for(cfg, 1), dev)
+    x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(sid, 0), dev)
+    q, s = quantised_weight(N, K, inputs.seed_for(sid, 1), dev)
     xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
     xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -190,14 +190,14 @@ def bench_linear_step(M, N, K, cfg, steps, warmup, dev, fmt="fp32"):
     return wall_ms, aq, gm, (x, q, s)
 
 
-def bench_linear_step_rotated(M, N, K, cfg, steps, warmup, dev):
+def bench_linear_step_rotated(M, N, K, sid, steps, warmup, dev):
     """The headline step with x and W cycled over enough copies that the
     Infinity Cache cannot hold them (the headline step reuses one x and one
     W, which stay cache-resident); graph-replayed."""
     copies = n_copies(2 * M * K + N * K)
-    xs = [inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 0) + 100 * c, dev)
+    xs = [inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(sid, 0) + 100 * c, dev)
           for c in range(copies)]
-    ws = [quantised_weight(N, K, inputs.seed_for(cfg, 1) + 100 * c, dev) for c in range(copies)]
+    ws = [quantised_weight(N, K, inputs.seed_for(sid, 1) + 100 * c, dev) for c in range(copies)]
     xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
     xsc = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -211,12 +211,12 @@ def bench_linear_step_rotated(M, N, K, cfg, steps, warmup, dev):
 
 
 def bench_decode(steps, warmup, dev, out):
-    cfg = inputs.CONFIGS[2]
+    cfg = inputs.DECODE
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    x = inputs.normal_bf16((M, K), 1.0, inputs.seed_for(2, 0), outlier_frac=0.01,
+    x = inputs.normal_bf16((M, K), 1.0, inputs.seed_for(inputs.SEED_DECODE, 0), outlier_frac=0.01,
                            outlier_mult=50.0).to(dev)
     copies = n_copies(N * K)
-    ws = [quantised_weight(N, K, inputs.seed_for(2, 1) + 100 * c, dev) for c in range(copies)]
+    ws = [quantised_weight(N, K, inputs.seed_for(inputs.SEED_DECODE, 1) + 100 * c, dev) for c in range(copies)]
     xq, xs = fp8bs.act_quant(x)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     us = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, ws[c][0], ws[c][1], y), copies, steps, warmup)
@@ -237,11 +237,11 @@ def bench_decode(steps, warmup, dev, out):
 
 
 def bench_act_quant(steps, warmup, dev, out):
-    for (M, K, fmt, cfg) in [(4096, 7168, "fp32", 3), (4096, 18432, "fp32", 3), (32768, 2048, "fp32", 4),
-                             (1024, 7168, "ue8m0", 5)]:
+    for (M, K, fmt, sid) in [(4096, 7168, "fp32", inputs.SEED_PREFILL), (4096, 18432, "fp32", inputs.SEED_PREFILL),
+                             (32768, 2048, "fp32", inputs.SEED_MOE), (1024, 7168, "ue8m0", inputs.SEED_UE8M0)]:
         nb = act_quant_bytes(M, K)
         copies = n_copies(nb)
-        xs_in = [inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 50 + c), dev)
+        xs_in = [inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(sid, 50 + c), dev)
                  for c in range(copies)]
         qs = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(copies)]
         ss = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
@@ -265,7 +265,7 @@ def bench_dequant(steps, warmup, dev, out):
     N, K = 18432, 7168
     nb = dequant_bytes(N, K)
     copies = n_copies(nb)
-    ws = [quantised_weight(N, K, inputs.seed_for(5, 1) + 100 * c, dev) for c in range(copies)]
+    ws = [quantised_weight(N, K, inputs.seed_for(inputs.SEED_UE8M0, 1) + 100 * c, dev) for c in range(copies)]
     ys = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     us = timed(lambda c: fp8bs.fp8bs_weight_dequant(ws[c][0], ws[c][1], ys[c]), copies, steps, warmup)
     out["weight_dequant_18432x7168"] = row_result("weight_dequant", us, None, nb, "hbm",
@@ -276,11 +276,11 @@ def bench_dequant(steps, warmup, dev, out):
 def bench_small_gemms(steps, warmup, dev, out):
     M = 1024
     for (N, K, tid) in [(1536, 7168, 2), (16384, 512, 4)]:
-        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(5, tid), dev)
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(inputs.SEED_UE8M0, tid), dev)
         xq, xs = fp8bs.act_quant(x, "ue8m0")
         nb = gemm_bytes(M, N, K)
         copies = n_copies(nb)
-        ws = [quantised_weight(N, K, inputs.seed_for(5, tid + 1) + 100 * c, dev) for c in range(copies)]
+        ws = [quantised_weight(N, K, inputs.seed_for(inputs.SEED_UE8M0, tid + 1) + 100 * c, dev) for c in range(copies)]
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         us = timed(lambda c: fp8bs.fp8bs_gemm(xq, xs, ws[c][0], ws[c][1], y), copies, steps, warmup)
         ai = 2 * M * N * K / nb
@@ -291,9 +291,9 @@ def bench_small_gemms(steps, warmup, dev, out):
 
 
 def bench_moe(steps, warmup, dev, out):
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
-    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(inputs.SEED_MOE, 9))
     off = torch.from_numpy(route["offsets"]).to(dev)
     R = int(route["offsets"][-1])
     active = int((route["counts"] > 0).sum())
@@ -301,13 +301,13 @@ def bench_moe(steps, warmup, dev, out):
     for proj, tid in (("up", 2), ("down", 3)):
         N, K = cfg[proj]["N"], cfg[proj]["K"]
         if proj == "up":
-            tok = inputs.normal_bf16_device((T, K), 1.0, inputs.seed_for(4, 0), dev)
+            tok = inputs.normal_bf16_device((T, K), 1.0, inputs.seed_for(inputs.SEED_MOE, 0), dev)
             x = tok.index_select(0, tok_idx)
             del tok
         else:
-            x = inputs.normal_bf16_device((R, K), 1.0, inputs.seed_for(4, 1), dev)
+            x = inputs.normal_bf16_device((R, K), 1.0, inputs.seed_for(inputs.SEED_MOE, 1), dev)
         xq, xs = fp8bs.act_quant(x)
-        w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(4, tid), dev)
+        w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(inputs.SEED_MOE, tid), dev)
         bq, bs = fp8bs.weight_quant(w)
         del w
         bq, bs = bq.view(E, N, K), bs.view(E, N // 128, K // 128)
@@ -324,9 +324,9 @@ def bench_moe_dispatch(steps, warmup, dev, out):
     (counting sort of the 4096 x 8 expert ids), the expert inputs (act_quant of
     each token written to its 8 routed rows) and the combine of the
     down-projection output [32768, 7168] into 4096 tokens."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
-    g = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    g = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(inputs.SEED_MOE, 9))
     idx = torch.from_numpy(g["choice"].astype(np.int32)).to(dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     row_token = torch.empty(T * topk, dtype=torch.int32, device=dev)
@@ -341,7 +341,7 @@ def bench_moe_dispatch(steps, warmup, dev, out):
     K, N = cfg["up"]["K"], cfg["down"]["N"]
     nb = 2 * T * K + R * K + 4 * R * (K // 128) + 4 * T * topk
     copies = n_copies(nb)
-    xs = [inputs.normal_bf16_device((T, K), 1.0, inputs.seed_for(4, 60 + c), dev) for c in range(copies)]
+    xs = [inputs.normal_bf16_device((T, K), 1.0, inputs.seed_for(inputs.SEED_MOE, 60 + c), dev) for c in range(copies)]
     qs = [torch.empty((R, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(copies)]
     ss = [torch.empty((R, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
     us = timed(lambda c: fp8bs.fp8bs_moe_quant_scatter(xs[c], row_of, qs[c], ss[c]), copies, steps,
@@ -351,8 +351,8 @@ def bench_moe_dispatch(steps, warmup, dev, out):
     del xs, qs, ss
     nb = 2 * R * N + 8 * T * topk + 2 * T * N
     copies = n_copies(nb)
-    outs = [inputs.normal_bf16_device((R, N), 1.0, inputs.seed_for(4, 70 + c), dev) for c in range(copies)]
-    w = torch.from_numpy(inputs.routing_weights(T, topk, inputs.seed_for(4, 6))).to(dev)
+    outs = [inputs.normal_bf16_device((R, N), 1.0, inputs.seed_for(inputs.SEED_MOE, 70 + c), dev) for c in range(copies)]
+    w = torch.from_numpy(inputs.routing_weights(T, topk, inputs.seed_for(inputs.SEED_MOE, 6))).to(dev)
     ys = [torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     us = timed(lambda c: fp8bs.fp8bs_moe_combine(outs[c], w, row_of, ys[c]), copies, steps, warmup)
     out[f"moe_combine_{R}x{N}_to_{T}"] = row_result("moe combine", us, None, nb, "hbm",
@@ -364,11 +364,12 @@ def bench_w8a16(steps, warmup, dev, out):
     """The BF16 path of the linear (weight dequantised in registers, bf16
     MFMA) on the prefill and decode shapes, against the bf16 MFMA peak (prefill)
     and HBM (decode)."""
-    for (M, N, K, cfg, bound) in [(4096, 18432, 7168, 3, "mfma_bf16"), (32, 18432, 7168, 2, "hbm")]:
-        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 20), dev)
+    for (M, N, K, sid, bound) in [(4096, 18432, 7168, inputs.SEED_PREFILL, "mfma_bf16"),
+                                  (32, 18432, 7168, inputs.SEED_DECODE, "hbm")]:
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(sid, 20), dev)
         nb = 2 * M * K + N * K + 4 * (-(-N // 128)) * (K // 128) + 2 * M * N
         copies = n_copies(N * K) if bound == "hbm" else 1
-        ws = [quantised_weight(N, K, inputs.seed_for(cfg, 21) + 100 * c, dev) for c in range(copies)]
+        ws = [quantised_weight(N, K, inputs.seed_for(sid, 21) + 100 * c, dev) for c in range(copies)]
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         us = timed(lambda c: fp8bs.fp8bs_w8a16_gemm(x, ws[c][0], ws[c][1], y), copies, steps, warmup)
         r = row_result(f"w8a16 gemm {M}x{N}x{K}", us, 2 * M * N * K, nb,
@@ -383,16 +384,16 @@ def bench_w8a16(steps, warmup, dev, out):
 def bench_ue8m0(steps, warmup, dev, out):
     """The ue8m0 fast path (power-of-two scales applied by the scaled MFMA) on
     the prefill GEMM and on the two GEMM shapes of the ue8m0 workload."""
-    for (M, N, K, cfg, tx, tw) in [(4096, 18432, 7168, 3, 0, 1), (1024, 1536, 7168, 5, 2, 3),
+    for (M, N, K, sid, tx, tw) in [(4096, 18432, 7168, inputs.SEED_PREFILL, 0, 1), (1024, 1536, 7168, inputs.SEED_UE8M0, 2, 3),
                                    (1024, 16384, 512, 5, 4, 5)]:
-        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, tx), dev)
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(sid, tx), dev)
         xq, xs = fp8bs.act_quant(x, "ue8m0")
         del x
         nb = gemm_bytes(M, N, K)
         copies = 1 if M == 4096 else n_copies(nb)
         ws = []
         for c in range(copies):
-            w = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(cfg, tw) + 100 * c, dev)
+            w = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(sid, tw) + 100 * c, dev)
             ws.append(fp8bs.weight_quant(w, "ue8m0"))
             del w
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -450,8 +451,8 @@ def bench_vendor(steps, warmup, dev, out):
     4096 x 16384 x 7168, whose 256 x 256 tiles fill whole rounds of the CUs."""
     one = torch.ones((), dtype=torch.float32, device=dev)
     for (M, N, K) in [(4096, 18432, 7168), (4096, 7168, 18432), (4096, 16384, 7168)]:
-        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(3, 20), dev)
-        w = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(3, 21), dev)
+        x = inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(inputs.SEED_PREFILL, 20), dev)
+        w = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(inputs.SEED_PREFILL, 21), dev)
         xq, xs = fp8bs.act_quant(x)
         xe, xse = fp8bs.act_quant(x, "ue8m0")
         wq, ws = fp8bs.weight_quant(w)
@@ -506,13 +507,14 @@ def cpu_baseline(x_dev, w_dev, budget_s, dev):
         log(f"  cpu {name:28s} {per_op[name]}")
 
     # act_quant, both formats (full tensors)
-    for (M, K, fmt, cfg) in [(4096, 7168, oracle.FMT_FP32, 3), (1024, 7168, oracle.FMT_UE8M0, 5),
-                             (32, 7168, oracle.FMT_FP32, 2)]:
-        xb = inputs.bf16_bits(inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(cfg, 50), dev).cpu())
+    for (M, K, fmt, sid) in [(4096, 7168, oracle.FMT_FP32, inputs.SEED_PREFILL),
+                             (1024, 7168, oracle.FMT_UE8M0, inputs.SEED_UE8M0),
+                             (32, 7168, oracle.FMT_FP32, inputs.SEED_DECODE)]:
+        xb = inputs.bf16_bits(inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(sid, 50), dev).cpu())
         dt = clock(lambda: oracle.act_quant(xb, fmt))
         op(f"act_quant_{M}x{K}_{'ue8m0' if fmt else 'fp32'}", dt, act_quant_bytes(M, K), "gbs", "whole")
     # weight_dequant [18432, 7168] (whole)
-    wq, ws = quantised_weight(18432, 7168, inputs.seed_for(5, 1), dev)
+    wq, ws = quantised_weight(18432, 7168, inputs.seed_for(inputs.SEED_UE8M0, 1), dev)
     q, sc = wq.view(torch.uint8).cpu().numpy(), ws.cpu().numpy()
     del wq, ws
     dt = clock(lambda: oracle.weight_dequant(q, sc))
@@ -521,23 +523,23 @@ def cpu_baseline(x_dev, w_dev, budget_s, dev):
     # decode GEMM and the two GEMMs of the ue8m0 workload (whole)
     for (M, N, K, fmt) in [(32, 18432, 7168, oracle.FMT_FP32), (1024, 1536, 7168, oracle.FMT_UE8M0),
                            (1024, 16384, 512, oracle.FMT_UE8M0)]:
-        xb = inputs.bf16_bits(inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(5, 2), dev).cpu())
-        wb = inputs.bf16_bits(inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(5, 3), dev).cpu())
+        xb = inputs.bf16_bits(inputs.normal_bf16_device((M, K), 1.0, inputs.seed_for(inputs.SEED_UE8M0, 2), dev).cpu())
+        wb = inputs.bf16_bits(inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(inputs.SEED_UE8M0, 3), dev).cpu())
         a, a_s = oracle.act_quant(xb, fmt)
         b, b_s = oracle.weight_quant(wb)
         dt = clock(lambda: oracle.gemm(a, a_s, b, b_s))
         op(f"gemm_{M}x{N}x{K}", dt, 2 * M * N * K, "gflops", "whole")
     # grouped MoE up projection on 16 of the 256 experts: every 16th in
     # order of row count, so the sample spans the Zipf distribution
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     E, T, topk, N, K = cfg["experts"], cfg["tokens"], cfg["topk"], cfg["up"]["N"], cfg["up"]["K"]
-    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(inputs.SEED_MOE, 9))
     counts = np.diff(route["offsets"])
     pick = np.sort(np.argsort(counts, kind="stable")[::16])
     rows = int(counts[pick].sum())
-    xb = inputs.bf16_bits(inputs.normal_bf16_device((rows, K), 1.0, inputs.seed_for(4, 0), dev).cpu())
+    xb = inputs.bf16_bits(inputs.normal_bf16_device((rows, K), 1.0, inputs.seed_for(inputs.SEED_MOE, 0), dev).cpu())
     a, a_s = oracle.act_quant(xb, oracle.FMT_FP32)
-    wb = inputs.bf16_bits(inputs.normal_bf16_device((len(pick) * N, K), 0.02, inputs.seed_for(4, 2),
+    wb = inputs.bf16_bits(inputs.normal_bf16_device((len(pick) * N, K), 0.02, inputs.seed_for(inputs.SEED_MOE, 2),
                                                     dev).cpu())
     b, b_s = oracle.weight_quant(wb)
     off = np.concatenate([[0], np.cumsum(counts[pick])]).astype(np.int32)
@@ -603,10 +605,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cfg = inputs.CONFIGS[3]
+    cfg = inputs.PREFILL
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     log(f"prefill fp8 linear M={M} N={N} K={K}: {args.warmup} warmup + {args.steps} timed steps")
-    wall_ms, aq_us, gm_us, prefill_inputs = bench_linear_step(M, N, K, 3, args.steps, args.warmup, dev)
+    wall_ms, aq_us, gm_us, prefill_inputs = bench_linear_step(M, N, K, inputs.SEED_PREFILL, args.steps, args.warmup, dev)
     flops = 2 * M * N * K
     value = flops / (wall_ms * 1e-3) / 1e12
     rows = {}
@@ -619,12 +621,12 @@ def main():
         set() if args.rows == "none" else set(args.rows.split(",")))
     if "down" in sel:
         d = cfg["down"]
-        w2, a2, g2, _ = bench_linear_step(d["M"], d["N"], d["K"], 3, args.steps, args.warmup, dev)
+        w2, a2, g2, _ = bench_linear_step(d["M"], d["N"], d["K"], inputs.SEED_PREFILL, args.steps, args.warmup, dev)
         rows["prefill_down_gemm_4096x7168x18432"] = row_result(
             "prefill down gemm", g2, 2 * d["M"] * d["N"] * d["K"], gemm_bytes(d["M"], d["N"], d["K"]),
             "mfma")
     if "rotated" in sel:
-        r_us, r_copies = bench_linear_step_rotated(M, N, K, 3, args.steps, args.warmup, dev)
+        r_us, r_copies = bench_linear_step_rotated(M, N, K, inputs.SEED_PREFILL, args.steps, args.warmup, dev)
         rows["prefill_linear_step_rotated"] = row_result(
             "prefill step, rotated", r_us, flops, act_quant_bytes(M, K) + gemm_bytes(M, N, K), "mfma",
             {"copies": r_copies})
@@ -688,7 +690,7 @@ def main():
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a row sample (~{args.cpu_seconds:.0f} s)")
         px, _, _ = prefill_inputs
-        w_bf16 = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(3, 1), dev)
+        w_bf16 = inputs.normal_bf16_device((N, K), 0.02, inputs.seed_for(inputs.SEED_PREFILL, 1), dev)
         result["cpu_baseline"] = cpu_baseline(px, w_bf16, args.cpu_seconds, dev)
     print(json.dumps(result), flush=True)
 

@@ -7,8 +7,10 @@ library's tests and the CPU oracle can take their inputs from it.
 Recipe
 ------
 * Base seed 965 (the seed the DeepSeek-V3 generate script fixes, per the
-  "DeepSeek-V3 User Guide", FAQ).  Tensor ``t`` of workload ``c`` uses
-  ``seed = 965 * 1000 + 10 * c + t``.
+  "DeepSeek-V3 User Guide", FAQ).  Tensor ``t`` of the workload with seed id
+  ``c`` uses ``seed = 965 * 1000 + 10 * c + t``; the ids are SEED_TINY (1),
+  SEED_DECODE (2), SEED_PREFILL (3), SEED_MOE (4), SEED_UE8M0 (5) and
+  SEED_MLA (6).
 * Normals are drawn in float32 with numpy's PCG64 (``standard_normal``),
   multiplied by the standard deviation, optionally given outliers, and then
   rounded to bfloat16 (round-to-nearest-even, torch's CPU cast).
@@ -32,8 +34,13 @@ import torch
 BASE_SEED = 965
 
 
-def seed_for(config: int, tensor: int) -> int:
-    return BASE_SEED * 1000 + 10 * int(config) + int(tensor)
+# Seed ids of the workloads (the c of the recipe above).
+SEED_TINY, SEED_DECODE, SEED_PREFILL, SEED_MOE, SEED_UE8M0, SEED_MLA = 1, 2, 3, 4, 5, 6
+
+
+def seed_for(workload: int, tensor: int) -> int:
+    """Seed of tensor `tensor` of the workload with seed id `workload`."""
+    return BASE_SEED * 1000 + 10 * int(workload) + int(tensor)
 
 
 def normal_f32(shape, std: float, seed: int, outlier_frac: float = 0.0,
@@ -102,23 +109,23 @@ def routing_weights(tokens: int, topk: int, seed: int) -> np.ndarray:
 
 # Workload shapes (rows of the hot-path scope table).  M, N, K follow
 # nn.Linear: x [M, K], W [N, K] (out x in).
-CONFIGS = {
-    1: dict(name="tiny fp8 linear", M=16, N=256, K=256, x_std=1.0, w_std=0.02, fmt="fp32"),
-    2: dict(name="decode weight-streaming fp8 linear", M=32, N=18432, K=7168, x_std=1.0,
-            w_std=0.02, outlier_frac=0.01, outlier_mult=50.0, fmt="fp32"),
-    3: dict(name="prefill fp8 linear (up and down)", M=4096, N=18432, K=7168, x_std=1.0,
-            w_std=0.02, down=dict(M=4096, N=7168, K=18432), fmt="fp32"),
-    4: dict(name="grouped MoE expert GEMM", tokens=4096, experts=256, topk=8, zipf_s=1.1,
-            up=dict(N=2048, K=7168), down=dict(N=7168, K=2048), x_std=1.0, w_std=0.02, fmt="fp32"),
-    5: dict(name="ue8m0 act_quant, weight_dequant, small-N and small-K GEMMs", M=1024, K=7168,
-            dequant=dict(N=18432, K=7168), gemms=[dict(N=1536, K=7168), dict(N=16384, K=512)],
-            x_std=1.0, w_std=0.02, fmt="ue8m0"),
-}
+TINY = dict(name="tiny fp8 linear", seed_id=SEED_TINY, M=16, N=256, K=256, x_std=1.0, w_std=0.02,
+            fmt="fp32")
+DECODE = dict(name="decode weight-streaming fp8 linear", seed_id=SEED_DECODE, M=32, N=18432, K=7168,
+              x_std=1.0, w_std=0.02, outlier_frac=0.01, outlier_mult=50.0, fmt="fp32")
+PREFILL = dict(name="prefill fp8 linear (up and down)", seed_id=SEED_PREFILL, M=4096, N=18432, K=7168,
+               x_std=1.0, w_std=0.02, down=dict(M=4096, N=7168, K=18432), fmt="fp32")
+MOE = dict(name="grouped MoE expert GEMM", seed_id=SEED_MOE, tokens=4096, experts=256, topk=8,
+           zipf_s=1.1, up=dict(N=2048, K=7168), down=dict(N=7168, K=2048), x_std=1.0, w_std=0.02,
+           fmt="fp32")
+UE8M0 = dict(name="ue8m0 act_quant, weight_dequant, small-N and small-K GEMMs", seed_id=SEED_UE8M0,
+             M=1024, K=7168, dequant=dict(N=18432, K=7168),
+             gemms=[dict(N=1536, K=7168), dict(N=16384, K=512)], x_std=1.0, w_std=0.02, fmt="ue8m0")
 
-# The MLA absorb products (workload id 6 in the seed recipe): the attention
+# The MLA absorb products (seed id SEED_MLA): the attention
 # shape the pages' configurations share (qk_nope_head_dim 128, v_head_dim 128,
 # kv_lora_rank 512) with the 671B model's 128 heads, wkv_b drawn like the other
 # weights (std 0.02) and N(0, 1) activations, at a decode batch of 32 tokens and
 # a 4096-token prefill.
 MLA = dict(name="MLA absorb with an FP8 wkv_b", heads=128, dn=128, dv=128, R=512,
-           decode_tokens=32, prefill_tokens=4096, x_std=1.0, w_std=0.02, seed_id=6)
+           decode_tokens=32, prefill_tokens=4096, x_std=1.0, w_std=0.02, seed_id=SEED_MLA)

@@ -184,8 +184,8 @@ def test_gemm_tail_split(M, N, K):
 def test_tiny_linear_end_to_end():
     """The tiny FP8 linear: x bf16 [16, 256] ~ N(0,1), W [256, 256] ~ N(0, 0.02)
     quantised to 2x2 blocks; act_quant on the GPU then the GEMM."""
-    x = inputs.normal_bf16((16, 256), 1.0, inputs.seed_for(1, 0))
-    w = inputs.normal_bf16((256, 256), 0.02, inputs.seed_for(1, 1))
+    x = inputs.normal_bf16((16, 256), 1.0, inputs.seed_for(inputs.SEED_TINY, 0))
+    w = inputs.normal_bf16((256, 256), 0.02, inputs.seed_for(inputs.SEED_TINY, 1))
     b, b_s = oracle.weight_quant(inputs.bf16_bits(w))
     y = fp8bs.linear(x.to(DEV), to_dev_u8(b), to_dev_f32(b_s), "fp32", torch.float32)
     torch.cuda.synchronize()
@@ -206,7 +206,7 @@ def sample_points(M, N, rng, n_random=4000):
     return np.array(rows, np.int64), np.array(cols, np.int64)
 
 
-def full_size_case(cfg, M, N, K, seed_x, seed_w, fmt=oracle.FMT_FP32, outliers=False, full=False):
+def full_size_case(M, N, K, seed_x, seed_w, fmt=oracle.FMT_FP32, outliers=False, full=False):
     x = inputs.normal_bf16((M, K), 1.0, seed_x, outlier_frac=0.01 if outliers else 0.0,
                            outlier_mult=50.0)
     w = inputs.normal_bf16((N, K), 0.02, seed_w)
@@ -234,18 +234,18 @@ def full_size_case(cfg, M, N, K, seed_x, seed_w, fmt=oracle.FMT_FP32, outliers=F
 
 def test_gemm_decode_full():
     """Decode-shaped: x [32, 7168] with 1% x50 outliers, W [18432, 7168]."""
-    full_size_case(2, 32, 18432, 7168, inputs.seed_for(2, 0), inputs.seed_for(2, 1), outliers=True,
+    full_size_case(32, 18432, 7168, inputs.seed_for(inputs.SEED_DECODE, 0), inputs.seed_for(inputs.SEED_DECODE, 1), outliers=True,
                    full=True)
 
 
 def test_gemm_prefill_up():
     """The prefill linear x [4096, 7168] . W [18432, 7168]^T, every output."""
-    full_size_case(3, 4096, 18432, 7168, inputs.seed_for(3, 0), inputs.seed_for(3, 1), full=True)
+    full_size_case(4096, 18432, 7168, inputs.seed_for(inputs.SEED_PREFILL, 0), inputs.seed_for(inputs.SEED_PREFILL, 1), full=True)
 
 
 def test_gemm_prefill_down():
     """The prefill down-projection x [4096, 18432] . W [7168, 18432]^T, every output."""
-    full_size_case(3, 4096, 7168, 18432, inputs.seed_for(3, 2), inputs.seed_for(3, 3), full=True)
+    full_size_case(4096, 7168, 18432, inputs.seed_for(inputs.SEED_PREFILL, 2), inputs.seed_for(inputs.SEED_PREFILL, 3), full=True)
 
 
 def test_gemm_prefill_outliers_full():
@@ -255,8 +255,8 @@ def test_gemm_prefill_outliers_full():
     the count of outputs that miss the plain bar 1e-2 |ref| + 1e-3 is
     printed and must stay a small fraction."""
     M, N, K = 4096, 18432, 7168
-    x = inputs.normal_bf16((M, K), 1.0, inputs.seed_for(3, 40), outlier_frac=0.01, outlier_mult=50.0)
-    w = inputs.normal_bf16((N, K), 0.02, inputs.seed_for(3, 41))
+    x = inputs.normal_bf16((M, K), 1.0, inputs.seed_for(inputs.SEED_PREFILL, 40), outlier_frac=0.01, outlier_mult=50.0)
+    w = inputs.normal_bf16((N, K), 0.02, inputs.seed_for(inputs.SEED_PREFILL, 41))
     b, b_s = oracle.weight_quant(inputs.bf16_bits(w))
     del w
     a, a_s = oracle.act_quant(inputs.bf16_bits(x), oracle.FMT_FP32)
@@ -282,7 +282,7 @@ def test_gemm_prefill_outliers_full():
 
 @pytest.mark.parametrize("N,K,tid", [(1536, 7168, 2), (16384, 512, 4)])
 def test_gemm_ue8m0_inputs(N, K, tid):
-    full_size_case(5, 1024, N, K, inputs.seed_for(5, tid), inputs.seed_for(5, tid + 1),
+    full_size_case(1024, N, K, inputs.seed_for(inputs.SEED_UE8M0, tid), inputs.seed_for(inputs.SEED_UE8M0, tid + 1),
                    fmt=oracle.FMT_UE8M0, full=True)
 
 
@@ -393,20 +393,20 @@ def test_moe_full_size(proj):
     the benchmark; the oracle quantises the same draw itself and the two are
     checked bit-exact; then every output of every expert (float32 and bf16)
     is compared with the oracle's grouped GEMM."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     E, T, topk = cfg["experts"], cfg["tokens"], cfg["topk"]
     N, K = (cfg["up"]["N"], cfg["up"]["K"]) if proj == "up" else (cfg["down"]["N"], cfg["down"]["K"])
-    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    route = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(inputs.SEED_MOE, 9))
     off = route["offsets"]
     R = int(off[-1])
     if proj == "up":
-        tok = inputs.normal_bf16((T, K), 1.0, inputs.seed_for(4, 0))
+        tok = inputs.normal_bf16((T, K), 1.0, inputs.seed_for(inputs.SEED_MOE, 0))
         x = tok[torch.from_numpy(route["token"])]
     else:
-        x = inputs.normal_bf16((R, K), 1.0, inputs.seed_for(4, 1))
+        x = inputs.normal_bf16((R, K), 1.0, inputs.seed_for(inputs.SEED_MOE, 1))
     a, a_s = oracle.act_quant(inputs.bf16_bits(x), 0)
     qd, sd = fp8bs.act_quant(x.to(DEV), 0)
-    w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(4, 2 if proj == "up" else 3), DEV)
+    w = inputs.normal_bf16_device((E * N, K), 0.02, inputs.seed_for(inputs.SEED_MOE, 2 if proj == "up" else 3), DEV)
     bq, bsq = fp8bs.weight_quant(w)
     offd = torch.from_numpy(off).to(DEV)
     c32 = fp8bs.moe_gemm(qd, sd, bq.view(E, N, K), bsq.view(E, N // 128, K // 128), offd, torch.float32)

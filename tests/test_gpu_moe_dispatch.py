@@ -62,10 +62,10 @@ def test_route_invalid_ids_and_empty():
 
 def test_route_full_size_zipf():
     """The MoE workload: 4096 tokens, top-8 of 256 experts, Zipf(1.1)."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     g = inputs.zipf_topk_routing(cfg["tokens"], cfg["experts"], cfg["topk"], cfg["zipf_s"],
-                                 inputs.seed_for(4, 9))
-    check_route(g["choice"].astype(np.int32), cfg["experts"], "route C4")
+                                 inputs.seed_for(inputs.SEED_MOE, 9))
+    check_route(g["choice"].astype(np.int32), cfg["experts"], "route, 4096 tokens top-8 of 256")
 
 
 def check_quant_scatter(T, topk, E, K, fmt, seed, outliers=False):
@@ -90,17 +90,17 @@ def test_quant_scatter_small(T, topk, E, K, fmt):
 
 def test_quant_scatter_full_size():
     """The MoE up-projection input: 4096 tokens x 7168, Zipf top-8 routing."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     g = inputs.zipf_topk_routing(cfg["tokens"], cfg["experts"], cfg["topk"], cfg["zipf_s"],
-                                 inputs.seed_for(4, 9))
+                                 inputs.seed_for(inputs.SEED_MOE, 9))
     ref_route = oracle.moe_route(g["choice"].astype(np.int32), cfg["experts"])
     R = int(ref_route["offsets"][-1])
-    x = inputs.normal_bf16((cfg["tokens"], cfg["up"]["K"]), 1.0, inputs.seed_for(4, 0))
+    x = inputs.normal_bf16((cfg["tokens"], cfg["up"]["K"]), 1.0, inputs.seed_for(inputs.SEED_MOE, 0))
     q, s = fp8bs.moe_quant_scatter(x.to(DEV), to_i32(ref_route["row_of"]), R, "fp32")
     torch.cuda.synchronize()
     qr, sr = oracle.moe_quant_scatter(inputs.bf16_bits(x), ref_route["row_of"], R, 0)
-    assert_bytes_equal(f32_bits(s), sr.view(np.uint32), "quant_scatter C4 scales")
-    assert_bytes_equal(u8(q), qr, "quant_scatter C4 codes")
+    assert_bytes_equal(f32_bits(s), sr.view(np.uint32), "quant_scatter 4096 tokens scales")
+    assert_bytes_equal(u8(q), qr, "quant_scatter 4096 tokens codes")
 
 
 def check_combine(out_bits: np.ndarray, w: np.ndarray, row_of: np.ndarray, what: str):
@@ -138,14 +138,14 @@ def test_combine_small(T, topk, E, N):
 
 def test_combine_full_size():
     """The MoE down-projection output [32768, 7168] combined into 4096 tokens."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.MOE
     T, topk, E, N = cfg["tokens"], cfg["topk"], cfg["experts"], cfg["down"]["N"]
-    g = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(4, 9))
+    g = inputs.zipf_topk_routing(T, E, topk, cfg["zipf_s"], inputs.seed_for(inputs.SEED_MOE, 9))
     r = oracle.moe_route(g["choice"].astype(np.int32), E)
     R = int(r["offsets"][-1])
-    out = inputs.bf16_bits(inputs.normal_bf16((R, N), 1.0, inputs.seed_for(4, 5)))
-    w = inputs.routing_weights(T, topk, inputs.seed_for(4, 6))
-    check_combine(out, w, r["row_of"], "combine C4")
+    out = inputs.bf16_bits(inputs.normal_bf16((R, N), 1.0, inputs.seed_for(inputs.SEED_MOE, 5)))
+    w = inputs.routing_weights(T, topk, inputs.seed_for(inputs.SEED_MOE, 6))
+    check_combine(out, w, r["row_of"], "combine 4096 tokens")
 
 
 def test_dispatch_gemm_combine_chain():

@@ -75,16 +75,16 @@ def test_act_quant_special_blocks(fmt):
     check_act_quant(_special_blocks(), fmt, f"act_quant special fmt={fmt}")
 
 
-@pytest.mark.parametrize("cfg,shape,fmt,outliers", [
-    (2, (32, 7168), 0, True),            # decode-shaped activations, 1% x50 outliers
-    (3, (4096, 7168), 0, False),         # prefill up-proj input
-    (3, (4096, 18432), 0, False),        # prefill down-proj input
-    (4, (32768, 2048), 0, False),        # MoE down-proj input
-    (5, (1024, 7168), 1, False),         # ue8m0
-    (5, (1024, 512), 1, False),          # ue8m0, K = 512 GEMM input
+@pytest.mark.parametrize("sid,shape,fmt,outliers", [
+    (inputs.SEED_DECODE, (32, 7168), 0, True),       # decode-shaped activations, 1% x50 outliers
+    (inputs.SEED_PREFILL, (4096, 7168), 0, False),   # prefill up-proj input
+    (inputs.SEED_PREFILL, (4096, 18432), 0, False),  # prefill down-proj input
+    (inputs.SEED_MOE, (32768, 2048), 0, False),      # MoE down-proj input
+    (inputs.SEED_UE8M0, (1024, 7168), 1, False),     # ue8m0
+    (inputs.SEED_UE8M0, (1024, 512), 1, False),      # ue8m0, K = 512 GEMM input
 ])
-def test_act_quant_full_size(cfg, shape, fmt, outliers):
-    x = inputs.normal_bf16(shape, 1.0, inputs.seed_for(cfg, 0),
+def test_act_quant_full_size(sid, shape, fmt, outliers):
+    x = inputs.normal_bf16(shape, 1.0, inputs.seed_for(sid, 0),
                            outlier_frac=0.01 if outliers else 0.0, outlier_mult=50.0)
     check_act_quant(x, fmt, f"act_quant{shape} fmt={fmt}")
 
@@ -104,7 +104,7 @@ def test_weight_quant_small(N, K):
 
 
 def test_weight_quant_full_size():
-    w = inputs.normal_bf16((18432, 7168), 0.02, inputs.seed_for(3, 1))
+    w = inputs.normal_bf16((18432, 7168), 0.02, inputs.seed_for(inputs.SEED_PREFILL, 1))
     check_weight_quant(w, "weight_quant[18432x7168]")
 
 
@@ -138,7 +138,7 @@ def test_weight_dequant_all_codes(N, K):
 def test_weight_dequant_full_size():
     """The ue8m0/dequant workload: W [18432, 7168] drawn N(0, 0.02) and
     quantised by the oracle, then expanded to bf16."""
-    w = inputs.normal_bf16((18432, 7168), 0.02, inputs.seed_for(5, 1))
+    w = inputs.normal_bf16((18432, 7168), 0.02, inputs.seed_for(inputs.SEED_UE8M0, 1))
     q, s = oracle.weight_quant(inputs.bf16_bits(w))
     check_dequant(q, s, "weight_dequant[18432x7168]")
 

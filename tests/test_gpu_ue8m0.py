@@ -116,7 +116,7 @@ def test_gemm_ue8m0_wide_exponents():
 def test_gemm_ue8m0_prefill_sampled():
     """The prefill shape 4096 x 18432 x 7168 with ue8m0 operands, sampled."""
     M, N, K = 4096, 18432, 7168
-    a, a_s, b, b_s = ue8m0_operands(M, N, K, inputs.seed_for(3, 30))
+    a, a_s, b, b_s = ue8m0_operands(M, N, K, inputs.seed_for(inputs.SEED_PREFILL, 30))
     c = fp8bs.fp8_gemm_ue8m0(to_dev_u8(a), to_dev_f32(a_s), to_dev_u8(b), to_dev_f32(b_s), torch.float32)
     torch.cuda.synchronize()
     rng = np.random.default_rng(31)

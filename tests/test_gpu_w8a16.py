@@ -71,20 +71,20 @@ def test_w8a16_wide_scales():
     check(run(x, q, s, torch.float32), ref, S, False, "w8a16 wide scales f32")
 
 
-@pytest.mark.parametrize("cfg,M,N,K", [
-    (3, 4096, 18432, 7168),      # prefill up-projection shape
-    (3, 4096, 7168, 18432),      # prefill down-projection shape
-    (2, 32, 18432, 7168),        # decode shape
-    (3, 4000, 18000, 1024),      # ragged M and N, with the launch split into 256x256 and 128x128 tiles
+@pytest.mark.parametrize("sid,M,N,K", [
+    (inputs.SEED_PREFILL, 4096, 18432, 7168),  # prefill up-projection shape
+    (inputs.SEED_PREFILL, 4096, 7168, 18432),  # prefill down-projection shape
+    (inputs.SEED_DECODE, 32, 18432, 7168),     # decode shape
+    (inputs.SEED_PREFILL, 4000, 18000, 1024),  # ragged M and N, the launch split into 256x256 and 128x128 tiles
 ])
-def test_w8a16_full_size_sampled(cfg, M, N, K):
+def test_w8a16_full_size_sampled(sid, M, N, K):
     """Full-size shapes (inputs drawn on the host and quantised by the oracle),
     checked at sampled points: whole rows, whole columns, tile corners and
     random points."""
-    x, q, s = operands(M, N, K, inputs.seed_for(cfg, 20))
+    x, q, s = operands(M, N, K, inputs.seed_for(sid, 20))
     c = fp8bs.w8a16_gemm(x.to(DEV), to_dev_u8(q), to_dev_f32(s), torch.float32)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cfg * 100 + N)
+    rng = np.random.default_rng(sid * 100 + N)
     rows = [0, M - 1, min(255, M - 1), min(256, M - 1)] + list(rng.integers(0, M, 2))
     # 16383 / 16384: the last column of the 256x256 launch and the first of the 128x128 one
     cols = [0, N - 1, 255, 256] + [c for c in (16383, 16384) if c < N] + list(rng.integers(0, N, 2))

@@ -467,7 +467,7 @@ def test_moe_route_matches_stable_sort(orc, T, topk, E, seed):
 
 
 def test_moe_route_distinct_experts_zipf(orc):
-    """The C4-style routing (distinct experts per token, Zipf-skewed): the
+    """The MoE workload's routing (distinct experts per token, Zipf-skewed): the
     sort reproduces the harness's own grouping by (expert, token)."""
     g = inputs.zipf_topk_routing(512, 64, 8, 1.1, 7)
     r = orc.moe_route(g["choice"].astype(np.int32), 64)
