@@ -251,7 +251,7 @@ def bench_act_quant(steps, warmup, dev, out):
         del xs_in, qs, ss
         # reference: a plain device copy moving the same bytes (half read, half
         # written), rotated and timed the same way -- what a streaming kernel of
-        # this size reaches on the box
+        # this size reaches on this GPU
         half = nb // 2 // 16 * 16
         srcs = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(copies)]
         dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(copies)]
