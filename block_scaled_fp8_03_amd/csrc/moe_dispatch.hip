@@ -7,8 +7,9 @@
 //
 //   route    stable counting sort of ids [T, topk] by expert -> offsets
 //            [E+1], row_token [R] and row_of [T, topk] (one launch each for
-//            chunk histograms, their scan, and the placement; no atomics, so
-//            the result is deterministic)
+//            chunk histograms, their scan, and the placement; the only
+//            atomics are LDS adds and ORs, whose order does not change the
+//            result, so it is deterministic)
 //   combine  y[t, :] = sum_k w[t, k] * out[row_of[t, k], :] in fp32, slot
 //            order, one rounding at the store
 // (The expert inputs -- act_quant of each token written to its routed rows --
@@ -45,8 +46,28 @@ __device__ __forceinline__ int load_chunk_ids(const int32_t* __restrict__ idx, i
   return n;
 }
 
+// Pass 1.  For E <= kCountLdsMaxE the chunk's ids go into an LDS histogram
+// with atomic adds (a count does not depend on the order of the adds, so the
+// table is deterministic); otherwise a thread owns experts e = tid, tid +
+// 256, ... and scans the chunk's ids from LDS.
+constexpr int kCountLdsMaxE = 8192;
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_count_kernel(
     const int32_t* __restrict__ idx, int64_t P, int E, int32_t* __restrict__ hist) {
+  if (E <= kCountLdsMaxE) {
+    __shared__ int32_t h[kCountLdsMaxE];
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) h[e] = 0;
+    __syncthreads();
+    const int64_t p0 = (int64_t)blockIdx.x * kRouteChunk;
+#pragma unroll
+    for (int i = threadIdx.x; i < kRouteChunk; i += kRouteThreads) {
+      const int id = p0 + i < P ? idx[p0 + i] : -1;
+      if (id >= 0 && id < E) atomicAdd(&h[id], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[(int64_t)blockIdx.x * E + e] = h[e];
+    return;
+  }
   __shared__ __attribute__((aligned(16))) int32_t ids[kRouteChunk];
   load_chunk_ids(idx, P, ids);
   const int4* ids4 = (const int4*)ids;
@@ -118,43 +139,46 @@ __global__ __launch_bounds__(kScanThreads) void moe_route_scan_kernel(int32_t* _
 }
 
 // Pair-parallel placement of one chunk, for E <= kFusedMaxE.  base[e] (LDS)
-// holds expert e's next free row; wcnt is LDS scratch [4][E].  The chunk goes
-// in rounds of 256 pairs, wave w taking pairs 64w .. 64w+63 of the round.  A
-// pair's row is base[id] + (pairs of the same expert in earlier waves of the
-// round) + (earlier lanes of its own wave with the same expert), found with
-// 63 lane shuffles; the per-wave counts come from LDS atomic adds, whose
-// order does not matter, so the placement is deterministic.
+// holds expert e's next free row; wmask is LDS scratch [4][E] of 64-bit lane
+// masks, zero on entry and on return.  The chunk goes in rounds of 256 pairs,
+// wave w taking pairs 64w .. 64w+63 of the round.  Each valid pair sets its
+// lane's bit in wmask[w][id] (an atomic OR: the result does not depend on the
+// order of the ORs, so the placement is deterministic).  A pair's row is then
+// base[id] + (pairs of the same expert in earlier waves of the round: the
+// popcounts of their masks) + (earlier lanes of its own wave with the same
+// expert: the popcount of its mask below its lane).
 constexpr int kFusedMaxE = 2048;
 
 __device__ void place_chunk(const int32_t* ids, int n, int64_t p0, int topk, int E, int32_t* base,
-                            int32_t* wcnt, int32_t* __restrict__ row_token,
+                            unsigned long long* wmask, int32_t* __restrict__ row_token,
                             int32_t* __restrict__ row_of) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long below = (1ull << lane) - 1;
   for (int r0 = 0; r0 < kRouteChunk; r0 += kRouteThreads) {
     const int i = r0 + threadIdx.x;
     const int id = i < n ? ids[i] : -1;
     const bool valid = id >= 0 && id < E;
-    int local = 0;
-    for (int d = 1; d < 64; ++d) {
-      const int other = __shfl(id, (lane - d) & 63);
-      local += (lane >= d && other == id) ? 1 : 0;
-    }
-    for (int j = threadIdx.x; j < 4 * E; j += kRouteThreads) wcnt[j] = 0;
-    __syncthreads();
-    if (valid) atomicAdd(&wcnt[wave * E + id], 1);
+    if (valid) atomicOr(&wmask[wave * E + id], 1ull << lane);
     __syncthreads();
     if (valid) {
-      int pos = base[id] + local;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w * E + id];
+      int pos = base[id] + __popcll(wmask[wave * E + id] & below);
+      for (int w = 0; w < wave; ++w) pos += __popcll(wmask[w * E + id]);
       const int64_t p = p0 + i;
       row_token[pos] = (int32_t)(p / topk);
       row_of[p] = pos;
     } else if (i < n) {
       row_of[p0 + i] = -1;
     }
-    __syncthreads();                                  // every lane has read base and wcnt
-    for (int e = threadIdx.x; e < E; e += kRouteThreads)
-      base[e] += wcnt[e] + wcnt[E + e] + wcnt[2 * E + e] + wcnt[3 * E + e];
+    __syncthreads();                                  // every lane has read base and wmask
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        c += __popcll(wmask[w * E + e]);
+        wmask[w * E + e] = 0;
+      }
+      base[e] += c;
+    }
     __syncthreads();
   }
 }
@@ -164,13 +188,17 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_place_kernel(
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
   __shared__ __attribute__((aligned(16))) int32_t ids[kRouteChunk];
   __shared__ int32_t base[kFusedMaxE];
-  __shared__ int32_t wcnt[4 * kFusedMaxE];
+  __shared__ unsigned long long wmask[4 * kFusedMaxE];
   const int n = load_chunk_ids(idx, P, ids);
   const int64_t p0 = (int64_t)blockIdx.x * kRouteChunk;
   if (E <= kFusedMaxE) {
-    for (int e = threadIdx.x; e < E; e += kRouteThreads) base[e] = first[(int64_t)blockIdx.x * E + e];
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+      base[e] = first[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) wmask[w * E + e] = 0;
+    }
     __syncthreads();
-    place_chunk(ids, n, p0, topk, E, base, wcnt, row_token, row_of);
+    place_chunk(ids, n, p0, topk, E, base, wmask, row_token, row_of);
     return;
   }
   // many experts: one thread per expert walks the chunk in order
@@ -202,7 +230,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scan_place_kernel(
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
   __shared__ __attribute__((aligned(16))) int32_t ids[kRouteChunk];
   __shared__ int32_t base[kFusedMaxE];
-  __shared__ int32_t wcnt[4 * kFusedMaxE];
+  __shared__ unsigned long long wmask[4 * kFusedMaxE];
   __shared__ int32_t part[kRouteThreads];
   __shared__ int32_t carry;
   const int c = blockIdx.x;
@@ -236,13 +264,15 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_scan_place_kernel(
     if (e < E) {
       base[e] = first + pre;
       if (c == 0) offsets[e] = first;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) wmask[w * E + e] = 0;
     }
     __syncthreads();                                   // every thread has read carry
     if (threadIdx.x == kRouteThreads - 1) carry += part[threadIdx.x];
     __syncthreads();
   }
   if (c == 0 && threadIdx.x == 0) offsets[E] = carry;
-  place_chunk(ids, n, (int64_t)c * kRouteChunk, topk, E, base, wcnt, row_token, row_of);
+  place_chunk(ids, n, (int64_t)c * kRouteChunk, topk, E, base, wmask, row_token, row_of);
 }
 
 int64_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
