@@ -169,7 +169,10 @@ __global__ void __launch_bounds__(64 * NWK) mla_key_kernel(MlaParams p) {
   load_tile(min(1, ntiles - 1), qr);
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One token tile; `next` stages the next tile and loads the one after it.
+  // The last tile is peeled off without them: its iteration then does not
+  // wait for a reload nobody reads before its barrier and stores.
+  auto iter = [&](int it, bool next) {
     const int b = it & 1;
     if (active) {
       const uint8_t* row = qs[b] + j * ROW_BYTES;
@@ -203,8 +206,10 @@ __global__ void __launch_bounds__(64 * NWK) mla_key_kernel(MlaParams p) {
         }
       }
     }
-    store_tile(b ^ 1, qr);
-    load_tile(min(it + 2, ntiles - 1), qr);
+    if (next) {
+      store_tile(b ^ 1, qr);
+      load_tile(min(it + 2, ntiles - 1), qr);
+    }
     __syncthreads();
     if (!OUT_F32) {
       // The staged tile out, two chunks per thread.  Chunks past R (idle
@@ -226,7 +231,9 @@ __global__ void __launch_bounds__(64 * NWK) mla_key_kernel(MlaParams p) {
         else *reinterpret_cast<v4u*>(dst) = v;
       }
     }
-  }
+  };
+  for (int it = 0; it + 1 < ntiles; ++it) iter(it, true);
+  iter(ntiles - 1, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -315,7 +322,9 @@ mla_value_kernel(MlaParams p) {
   load_tile(min(1, ntiles - 1), xr);
   __syncthreads();
 
-  for (int i = 0; i < ntiles; ++i) {
+  // One token tile; the last is peeled off without staging or loading a
+  // next one (as in the key kernel).
+  auto iter = [&](int i, bool next) {
     const int b = i & 1;
     if (active) {
       const uint8_t* row = xs[b] + j * ROW_BYTES;
@@ -349,8 +358,10 @@ mla_value_kernel(MlaParams p) {
     }
     // the next tile into the other buffer (last read one iteration ago, behind
     // the barrier that ended it), then the loads of the tile after it
-    store_tile(b ^ 1, xr);
-    load_tile(min(i + 2, ntiles - 1), xr);
+    if (next) {
+      store_tile(b ^ 1, xr);
+      load_tile(min(i + 2, ntiles - 1), xr);
+    }
     __syncthreads();
     if (!OUT_F32) {
       // the staged tile out, one chunk per thread, clamped as in the key
@@ -364,7 +375,9 @@ mla_value_kernel(MlaParams p) {
       const v4u v = *reinterpret_cast<const v4u*>(&os[b][r * (OCPR * 16) + ((ch ^ (r & (OCPR - 1))) << 4)]);
       *reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(p.out) + ((size_t)tr * p.H + h) * p.dv + cbase + 8 * ch) = v;
     }
-  }
+  };
+  for (int i = 0; i + 1 < ntiles; ++i) iter(i, true);
+  iter(ntiles - 1, false);
 }
 
 // Token chunking, evenly split, a multiple of 16: the largest chunk of 1024,
