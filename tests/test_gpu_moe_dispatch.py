@@ -44,6 +44,9 @@ def check_route(idx: np.ndarray, E: int, what: str):
     (2000, 2, 3000, 4),                               # experts > one scan round (3 launches)
     (513, 1, 7, 5),                                   # one pair past a chunk boundary
     (20000, 8, 256, 6),                               # count table too big to fuse (3 launches)
+    (600, 8, 1, 7),                                   # one expert: every lane mask full
+    (300, 4, 8192, 8),                                # largest E of the LDS-histogram count
+    (300, 4, 8193, 9),                                # E past it: thread-per-expert count
 ])
 def test_route_random(T, topk, E, seed):
     rng = np.random.default_rng(seed)
