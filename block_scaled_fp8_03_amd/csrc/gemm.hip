@@ -1364,19 +1364,31 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   // The main tile: 256 x 256, eight waves of 128 (m) x 64 (n), two LDS
   // stages, the conflict-free swizzle (ue8m0: four waves of 128 x 128).
   constexpr int BM = 256, BN = 256;
-  // Smaller GEMMs whose 256 x 256 tiles cannot fill the CUs run on 128 x 128
-  // tiles when those give at least one tile per two CUs, else on 64 x 64
-  // tiles with four LDS stages, two workgroups per CU (measured: 1024 x 1536
-  // x 7168 104 -> 30 us against one 256 x 256 tile per CU, then 30.2 -> 27.9
-  // us with four stages instead of three; these tiles are bound by operand
-  // fetch, 17 KB per 1 MFLOP K block).
+  // Smaller GEMMs whose 256 x 256 tiles cannot fill the CUs, by their count
+  // of 128 x 128 tiles t:
+  //   t <= CUs / 2 ... 64 x 64 tiles, four LDS stages, two workgroups per CU
+  //     (measured: 1024 x 1536 x 7168 104 -> 30 us against one 256 x 256 tile
+  //     per CU, then 30.2 -> 27.9 us with four stages instead of three; these
+  //     tiles are bound by operand fetch, 17 KB per 1 MFLOP K block);
+  //   t <= CUs ....... 128 x 128 tiles, three stages, one workgroup per CU;
+  //   t <= 2 CUs ..... 128 x 128 tiles, two stages, two workgroups per CU: one
+  //     round instead of two (M x 18432 x 7168, us: M = 192 87.7 -> 69.6,
+  //     256 90.0 -> 79.0, 384 92.5 -> 76.1);
+  //   beyond ......... the 256 x 256 tiles below, one partial round (M = 512:
+  //     135.0 -> 107.1 us against three rounds of 128 x 128 tiles).
   const int cus = device_cus();
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (tiles(BM, BN) < cus) {
-    if (tiles(128, 128) >= cus / 2) {
+  if (tiles(BM, BN) < cus && tiles(128, 128) <= 2 * cus) {
+    const int t128 = tiles(128, 128);
+    if (t128 > cus) {
       p.num_m = (int)((M + 127) / 128);
       p.num_n = (int)((N + 127) / 128);
-      return run_tile<128, 128, 64, 64, 3, 4, 2, 1, E8>(p, out_f32, p.num_m * p.num_n, stream);
+      return run_tile<128, 128, 64, 64, 2, 4, 2, 2, E8>(p, out_f32, t128, stream);
+    }
+    if (t128 >= cus / 2) {
+      p.num_m = (int)((M + 127) / 128);
+      p.num_n = (int)((N + 127) / 128);
+      return run_tile<128, 128, 64, 64, 3, 4, 2, 1, E8>(p, out_f32, t128, stream);
     }
     p.num_m = (int)((M + 63) / 64);
     p.num_n = (int)((N + 63) / 64);

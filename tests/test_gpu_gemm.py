@@ -50,10 +50,14 @@ SMALL = [(16, 256, 256), (1, 1, 128), (5, 7, 128), (33, 130, 256), (64, 64, 128)
     (1000, 2100, 640),    # 128 x 128 tiles, per-stage a_s (K/128 = 5)
     (2050, 8200, 384),    # 256 x 256 tiles, per-stage a_s, ragged M and N
     (2050, 8200, 1024),   # 256 x 256 tiles, a_s in chunks, ragged M and N
+    (300, 12000, 1536),   # 128 x 128 tiles, two workgroups per CU (282 tiles), ragged
+    (300, 12000, 640),    # the same with per-stage a_s
+    (520, 14000, 640),    # 256 x 256 tiles in one partial round (550 of 128 x 128), ragged
 ])
 def test_gemm_tile_configs(M, N, K):
-    """Shapes that select each tile size of the dense path (the 64 x 64 one is
-    taken by the small shapes above), with ragged edges, compared in full."""
+    """Shapes that select each tile size of the dense path on a 256-CU GPU (the
+    64 x 64 one is taken by the small shapes above), with ragged edges, compared
+    in full."""
     a, a_s, b, b_s = rand_operands(M, N, K, 5000 + M + N + K)
     ref = oracle.gemm(a, a_s, b, b_s)
     assert_close(run_gemm(a, a_s, b, b_s, torch.float32), ref, f"gemm[{M}x{N}x{K}] f32")
