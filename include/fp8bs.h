@@ -264,7 +264,8 @@ int64_t fp8bs_moe_route_workspace_size(int64_t T, int64_t topk, int64_t E);
  *                   id lies in [0, E)
  *   row_token  out  DEVICE int32 [T*topk]: the token of each row r < R, rows
  *                   of one expert in (token, slot) order (the order the
- *                   pages' torch.where yields); entries >= R untouched
+ *                   pages' per-expert index lookup yields); entries >= R
+ *                   untouched
  *   row_of     out  DEVICE int32 [T, topk]: the row of each (token, slot), or
  *                   -1 when its id is outside [0, E) (such a pair is not
  *                   routed and takes no row)

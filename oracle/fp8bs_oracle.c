@@ -426,9 +426,9 @@ void orc_mla_absorb_points(int side, const uint16_t* in, const uint8_t* w, const
 
 /* ------------------------------------------------------------------------ */
 /* MoE dispatch and combine around the expert GEMMs (Admin guide 6.4 and     */
-/* 8.4: per-expert hit counts by bincount; for each expert with hits, the     */
-/* (token, slot) pairs whose routed expert it is, in token order as          */
-/* torch.where yields them; the expert runs on those tokens' rows; its output */
+/* 8.4: per-expert hit counts; for each expert with hits, the (token, slot)  */
+/* pairs whose routed expert it is, in token order as the pages' index       */
+/* lookup yields them; the expert runs on those tokens' rows; its output     */
 /* is scaled by the routing weight of that (token, slot) and summed into the */
 /* token's output, which starts at zero).                                     */
 /* ------------------------------------------------------------------------ */
