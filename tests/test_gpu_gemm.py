@@ -53,6 +53,8 @@ SMALL = [(16, 256, 256), (1, 1, 128), (5, 7, 128), (33, 130, 256), (64, 64, 128)
     (300, 12000, 1536),   # 128 x 128 tiles, two workgroups per CU (282 tiles), ragged
     (300, 12000, 640),    # the same with per-stage a_s
     (520, 14000, 640),    # 256 x 256 tiles in one partial round (550 of 128 x 128), ragged
+    (300, 12000, 128),    # two workgroups per CU, a single K block
+    (520, 14000, 128),    # one partial round of 256 x 256 tiles, a single K block
 ])
 def test_gemm_tile_configs(M, N, K):
     """Shapes that select each tile size of the dense path on a 256-CU GPU (the
