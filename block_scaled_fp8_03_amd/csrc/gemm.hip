@@ -1370,7 +1370,9 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   //     (measured: 1024 x 1536 x 7168 104 -> 30 us against one 256 x 256 tile
   //     per CU, then 30.2 -> 27.9 us with four stages instead of three; these
   //     tiles are bound by operand fetch, 17 KB per 1 MFLOP K block);
-  //   t <= CUs ....... 128 x 128 tiles, three stages, one workgroup per CU;
+  //   t <= CUs ....... 128 x 128 tiles, four stages, one workgroup per CU
+  //     (three in flight: M x 18432 x 7168, M = 65 41.4 -> 39.9 us against
+  //     three stages, 1000 x 2100 x 7168 42.2 -> 40.7 us);
   //   t <= 2 CUs ..... 128 x 128 tiles, two stages, two workgroups per CU: one
   //     round instead of two (M x 18432 x 7168, us: M = 192 87.7 -> 69.6,
   //     256 90.0 -> 79.0, 384 92.5 -> 76.1);
@@ -1388,7 +1390,7 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
     if (t128 >= cus / 2) {
       p.num_m = (int)((M + 127) / 128);
       p.num_n = (int)((N + 127) / 128);
-      return run_tile<128, 128, 64, 64, 3, 4, 2, 1, E8>(p, out_f32, t128, stream);
+      return run_tile<128, 128, 64, 64, 4, 4, 2, 1, E8>(p, out_f32, t128, stream);
     }
     p.num_m = (int)((M + 63) / 64);
     p.num_n = (int)((N + 63) / 64);
