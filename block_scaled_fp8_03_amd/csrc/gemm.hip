@@ -1496,7 +1496,8 @@ hipError_t run_w8a16(GemmParams p, bool out_f32, hipStream_t stream) {
 
 // Tile choice: decode-sized M streams the weight through 64-column tiles
 // (two workgroups per CU, six stages); GEMMs whose 256 x 256 tiles cannot
-// fill the CUs use 128 x 128 tiles, one workgroup per CU while those fit the
+// fill the CUs use 64-row tiles while 128 x 128 ones would not reach half
+// the CUs, then 128 x 128 tiles, one workgroup per CU while those fit the
 // CUs and two per CU (three stages) up to twice that (one round instead of
 // two: M x 18432 x 7168, M = 192 166.2 -> 101.1 us, 256 166.4 -> 103.9, 384
 // 173.8 -> 118.4); beyond, and for the rest, the 256 x 256 eight-wave tile
@@ -1526,6 +1527,9 @@ hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, voi
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < cus) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    // too few 128 x 128 tiles for half the CUs: the 64-row tiles, two per CU
+    // (128 x 7168 x 18432 208.7 -> 109.6 us, 100 x 4096 x 7168 83.2 -> 43.7)
+    if (t128 < cus / 2) return run_w8a16<64, 64, 64, 16, 4, 6, 2>(p, out_f32, stream);
     if (t128 <= cus) return run_w8a16<128, 128, 64, 64, 4, 4, 1>(p, out_f32, stream);
     if (t128 <= 2 * cus) return run_w8a16<128, 128, 64, 64, 4, 3, 2>(p, out_f32, stream);
   }
