@@ -1366,10 +1366,13 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
   constexpr int BM = 256, BN = 256;
   // Smaller GEMMs whose 256 x 256 tiles cannot fill the CUs, by their count
   // of 128 x 128 tiles t:
-  //   t <= CUs / 2 ... 64 x 64 tiles, four LDS stages, two workgroups per CU
-  //     (measured: 1024 x 1536 x 7168 104 -> 30 us against one 256 x 256 tile
-  //     per CU, then 30.2 -> 27.9 us with four stages instead of three; these
-  //     tiles are bound by operand fetch, 17 KB per 1 MFLOP K block);
+  //   t < CUs / 2, or 64 x 64 tiles that fit one round at two per CU ...
+  //     64 x 64 tiles, four LDS stages, two workgroups per CU (measured:
+  //     1024 x 1536 x 7168 104 -> 30 us against one 256 x 256 tile per CU,
+  //     then 30.2 -> 27.9 us with four stages instead of three; these tiles
+  //     are bound by operand fetch, 17 KB per 1 MFLOP K block; at t = CUs / 2
+  //     they beat half the CUs on 128 x 128 tiles: 512 x 4096 x 7168 40.3 ->
+  //     34.6 us, 512 x 4096 x 2048 14.3 -> 10.2 us);
   //   t <= CUs ....... 128 x 128 tiles, four stages, one workgroup per CU
   //     (three in flight: M x 18432 x 7168, M = 65 41.4 -> 39.9 us against
   //     three stages, 1000 x 2100 x 7168 42.2 -> 40.7 us);
@@ -1387,7 +1390,7 @@ hipError_t dense_gemm(const void* a, const float* a_s, const void* b, const floa
       p.num_n = (int)((N + 127) / 128);
       return run_tile<128, 128, 64, 64, 2, 4, 2, 2, E8>(p, out_f32, t128, stream);
     }
-    if (t128 >= cus / 2) {
+    if (t128 >= cus / 2 && tiles(64, 64) > 2 * cus) {
       p.num_m = (int)((M + 127) / 128);
       p.num_n = (int)((N + 127) / 128);
       return run_tile<128, 128, 64, 64, 4, 4, 2, 1, E8>(p, out_f32, t128, stream);
@@ -1527,9 +1530,11 @@ hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, voi
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < cus) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    // too few 128 x 128 tiles for half the CUs: the 64-row tiles, two per CU
-    // (128 x 7168 x 18432 208.7 -> 109.6 us, 100 x 4096 x 7168 83.2 -> 43.7)
-    if (t128 < cus / 2) return run_w8a16<64, 64, 64, 16, 4, 6, 2>(p, out_f32, stream);
+    // too few 128 x 128 tiles for half the CUs, or 64-row tiles that fit one
+    // round at two per CU: the 64-row tiles (128 x 7168 x 18432 208.7 ->
+    // 109.6 us, 100 x 4096 x 7168 83.2 -> 43.7, 512 x 4096 x 7168 86.7 -> 56.5)
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    if (t128 < cus / 2 || t64 <= 2 * cus) return run_w8a16<64, 64, 64, 16, 4, 6, 2>(p, out_f32, stream);
     if (t128 <= cus) return run_w8a16<128, 128, 64, 64, 4, 4, 1>(p, out_f32, stream);
     if (t128 <= 2 * cus) return run_w8a16<128, 128, 64, 64, 4, 3, 2>(p, out_f32, stream);
   }

@@ -55,6 +55,7 @@ SMALL = [(16, 256, 256), (1, 1, 128), (5, 7, 128), (33, 130, 256), (64, 64, 128)
     (520, 14000, 640),    # 256 x 256 tiles in one partial round (550 of 128 x 128), ragged
     (300, 12000, 128),    # two workgroups per CU, a single K block
     (520, 14000, 128),    # one partial round of 256 x 256 tiles, a single K block
+    (500, 4000, 1536),    # 128 x 128 tiles for half the CUs: 64 x 64 ones instead (512)
 ])
 def test_gemm_tile_configs(M, N, K):
     """Shapes that select each tile size of the dense path on a 256-CU GPU (the

@@ -46,6 +46,7 @@ def check(got, ref, S, bf16, what):
     (48, 300, 384), (64, 129, 256),                       # 64-row decode tiles
     (65, 200, 384), (257, 129, 256), (300, 520, 1024), (513, 300, 640),   # 64-row tiles (few 128 x 128)
     (100, 18000, 256),                                    # 128 x 128 tiles, one per CU (141)
+    (500, 4000, 640),                                     # 64-row tiles in one round (512)
     (2050, 8200, 256),                                    # 256 x 256 tiles, ragged M and N
     (300, 12000, 640),                                    # 128 x 128, two per CU (282 tiles)
     (520, 14000, 256),                                    # 256 x 256 tiles, one partial round
