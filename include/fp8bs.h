@@ -271,7 +271,7 @@ int64_t fp8bs_moe_route_workspace_size(int64_t T, int64_t topk, int64_t E);
  *                   routed and takes no row)
  *   workspace  tmp  DEVICE, >= fp8bs_moe_route_workspace_size bytes, 4-byte
  *                   aligned; its contents are scratch (nothing needs clearing)
- *   T >= 0, 1 <= topk, 1 <= E, T*topk < 2^31.  Two kernel launches (three
+ *   T >= 0, 1 <= topk, 1 <= E, T*topk < 2^31.  Two kernel launches (four
  *   when ceil(T*topk/512) * E > 65536 or E > 2048); the result does not
  *   depend on timing (its only atomics are on-chip adds and ORs, whose order
  *   does not change it).
