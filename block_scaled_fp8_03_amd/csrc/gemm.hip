@@ -362,9 +362,11 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// m tiles of an expert with n_rows rows in class `large`.
-__device__ __forceinline__ int class_mtiles(int n_rows, bool large) {
-  return large ? (n_rows > kMoeSplit ? (n_rows + 255) / 256 : 0) : ((n_rows > 0 && n_rows <= kMoeSplit) ? 1 : 0);
+// m tiles of an expert with n_rows rows in class `large` (large tiles of
+// 1 << lsh rows).
+__device__ __forceinline__ int class_mtiles(int n_rows, bool large, int lsh) {
+  return large ? (n_rows > kMoeSplit ? (n_rows + (1 << lsh) - 1) >> lsh : 0)
+               : ((n_rows > 0 && n_rows <= kMoeSplit) ? 1 : 0);
 }
 
 // Rows of the experts e0 + 64 j + lane (j < 4), ranges clamped to [0, R]
@@ -390,9 +392,15 @@ template <bool ASCH, bool OUT_F32>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 moe_gemm_kernel(GemmParams p) {
   constexpr int LB = tile_lds_bytes<256, 256, 2, 8, ASCH>(), SB = tile_lds_bytes<64, 256, 3, 8, ASCH>();
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LB > SB ? LB : SB];
+  constexpr int ST64 = ASCH ? 7 : 6, ST128 = ASCH ? 5 : 4;   // narrow small-expert tiles' stages
+  constexpr int S64 = tile_lds_bytes<64, 64, ST64, 8, ASCH>(), S128 = tile_lds_bytes<64, 128, ST128, 8, ASCH>();
+  constexpr int L128 = tile_lds_bytes<128, 128, 3, 8, ASCH>();
+  static_assert(S64 <= LB && S128 <= LB && SB <= LB && L128 <= LB, "the 256 x 256 layout is the largest");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LB];
   const int lane = threadIdx.x & 63;
-  const int nn = p.num_n;
+  const int lsh = p.large_sh;                             // large tiles: 1 << lsh square
+  const int nn = (p.N + (1 << lsh) - 1) >> lsh;           // large tiles' n tiles
+  const int nns = (p.N + p.small_bn - 1) / p.small_bn;    // small tiles' n tiles
 
   // real m tiles of each class (the first 256 experts' row counts are kept)
   int rows0[4];
@@ -409,14 +417,14 @@ moe_gemm_kernel(GemmParams p) {
     int cl = 0, cs = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      cl += class_mtiles(rows[j], true);
-      cs += class_mtiles(rows[j], false);
+      cl += class_mtiles(rows[j], true, lsh);
+      cs += class_mtiles(rows[j], false, lsh);
     }
     ml += __shfl(wave_incl_scan(cl, lane), 63);
     ms += __shfl(wave_incl_scan(cs, lane), 63);
   }
   const int64_t L = (int64_t)__builtin_amdgcn_readfirstlane(ml) * nn;
-  const int64_t S = (int64_t)__builtin_amdgcn_readfirstlane(ms) * nn;
+  const int64_t S = (int64_t)__builtin_amdgcn_readfirstlane(ms) * nns;
 
   // this XCD's parts of both lists and this workgroup's place in its sequence
   const int x = blockIdx.x % 8, k = blockIdx.x / 8;
@@ -434,7 +442,8 @@ moe_gemm_kernel(GemmParams p) {
     large = false;
     idx = s0 + (k - lx);
   }
-  const int nt = (int)(idx % nn), gm = (int)(idx / nn);
+  const int nc = large ? nn : nns;
+  const int nt = (int)(idx % nc), gm = (int)(idx / nc);
 
   // the expert and m tile of class m tile gm: experts in index order, so
   // expert e0 + 64 j + lane comes after all of chunk j - 1 of its 256
@@ -449,7 +458,7 @@ moe_gemm_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int cnt = class_mtiles(rows[j], large);
+      const int cnt = class_mtiles(rows[j], large, lsh);
       const int incl = wave_incl_scan(cnt, lane);
       const int excl = before + incl - cnt;
       const unsigned long long ball = __ballot(gm >= excl && gm < excl + cnt);
@@ -473,13 +482,25 @@ moe_gemm_kernel(GemmParams p) {
   // skips the MFMAs of the empty half (in the Zipf routing of the 4096-token
   // workload, 57 of 155 such m tiles; up 1013 -> 963-979 us, down 1086-1097 ->
   // 1038-1067 us, same box, bit-identical).
-  if (large) {
+  if (large && lsh == 7) {
+    // few experts: 128 x 128 tiles (eight waves of 64 x 32), HALF when the
+    // m tile holds at most 64 rows
+    if (hi - (lo + mt * 128) > 64)
+      gemm_tile<128, 128, 64, 32, 3, 8, 2, ASCH, OUT_F32, false, false>(p, smem, lo + mt * 128, hi, nt * 128, B, Bs);
+    else
+      gemm_tile<128, 128, 64, 32, 3, 8, 2, ASCH, OUT_F32, false, false, true>(p, smem, lo + mt * 128, hi, nt * 128,
+                                                                             B, Bs);
+  } else if (large) {
     if (hi - (lo + mt * 256) > 128)
       gemm_tile<256, 256, 128, 64, 2, 8, 2, ASCH, OUT_F32, false, false>(p, smem, lo + mt * 256, hi, nt * 256, B, Bs);
     else
       gemm_tile<256, 256, 128, 64, 2, 8, 2, ASCH, OUT_F32, false, false, true>(p, smem, lo + mt * 256, hi, nt * 256,
                                                                               B, Bs);
   }
+  else if (p.small_bn == 64)
+    gemm_tile<64, 64, 32, 16, ST64, 8, 2, ASCH, OUT_F32, true, false>(p, smem, lo, hi, nt * 64, B, Bs);
+  else if (p.small_bn == 128)
+    gemm_tile<64, 128, 32, 32, ST128, 8, 2, ASCH, OUT_F32, true, false>(p, smem, lo, hi, nt * 128, B, Bs);
   else
     gemm_tile<64, 256, 64, 32, 3, 8, 2, ASCH, OUT_F32, true, false>(p, smem, lo, hi, nt * 256, B, Bs);
 }
@@ -1459,14 +1480,31 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   GemmParams p{};
   p.a = (const uint8_t*)a; p.a_s = a_s; p.b = (const uint8_t*)b; p.b_s = b_s; p.c = c;
   p.offsets = offsets; p.rows = (int)R; p.N = (int)N; p.K = (int)K; p.E = (int)E;
-  p.num_n = (int)((N + 255) / 256);
+  // Few experts: the small-expert tiles are 64 or 128 columns wide when even
+  // every expert holding rows would give no more such tiles than CUs, so the
+  // weight stream spreads over more CUs in one round.  A narrow tile streams
+  // less per CU than a 64 x 256 one (its fixed per-K-block cost is spread
+  // over fewer bytes), so it pays only when it needs no second round:
+  // 8 experts x 16 rows, N = 2048, K = 7168: 57.0 -> 36.4 us with 64-column
+  // tiles, while 31 experts went 78.8 -> 139.3 us when they took four rounds.
+  const int64_t cus = device_cus();
+  p.small_bn = E * ((N + 63) / 64) <= cus ? 64 : E * ((N + 127) / 128) <= cus ? 128 : 256;
+  const int64_t nns = (N + p.small_bn - 1) / p.small_bn;
   // Upper bounds on each class's m tiles: the large experts' sum of
-  // ceil(rows / 256) <= R / 256 + (number of such experts), with at most
+  // ceil(rows / side) <= R / side + (number of such experts), with at most
   // R / (kMoeSplit + 1) of them; one small tile per expert with rows.
-  const int64_t ml = R / 256 + std::min<int64_t>(E, R / (kMoeSplit + 1));
+  const int64_t nlarge = std::min<int64_t>(E, R / (kMoeSplit + 1));
+  // The large experts' tiles are 128 x 128 when there can be no more than
+  // two rounds of them (N = 2048, K = 7168, us: 8 experts x 200 rows 90.8 ->
+  // 53.2, 4 x 300 88.4 -> 45.9, 16 x 100 71.4 -> 55.1), else 256 x 256: with
+  // more 128 x 128 rounds the narrower tiles lose (12 x 300 94.9 -> 117.9,
+  // 8 x 700 97.2 -> 130.9).
+  p.large_sh = (R / 128 + nlarge) * ((N + 127) / 128) <= 2 * cus ? 7 : 8;
+  const int64_t ml = (R >> p.large_sh) + nlarge;
+  p.num_n = (int)((N + (1 << p.large_sh) - 1) >> p.large_sh);
   const int64_t ms = std::min<int64_t>(E, R);
   // each XCD's part of a class list is at most ceil(tiles / 8)
-  const int64_t grid = 8 * ((ml * p.num_n + 7) / 8 + (ms * p.num_n + 7) / 8);
+  const int64_t grid = 8 * ((ml * p.num_n + 7) / 8 + (ms * nns + 7) / 8);
   const bool chunked = (K / 128) % 4 == 0 && ((uintptr_t)a_s & 15) == 0;
   const dim3 g((unsigned)grid), blk(512);
   if (chunked) {

@@ -125,6 +125,8 @@ struct GemmParams {
   int num_m;              // dense: m tiles
   int num_n;              // n tiles
   int n0;                 // dense: first output column of this launch's tiles (a multiple of 128)
+  int small_bn;           // MoE: column width of the small-expert tiles (64, 128 or 256)
+  int large_sh;           // MoE: log2 of the large-expert tiles' side (8: 256 x 256, 7: 128 x 128)
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so

@@ -351,8 +351,11 @@ def _moe_operands_from_counts(counts, N, K, seed):
 
 @pytest.mark.parametrize("name,E,N,K,seed", [
     ("mixed, E > 4 x 64", 300, 512, 256, 1),   # both classes; expert scan over five 64-lane chunks
-    ("small only", 17, 768, 384, 2),          # every expert <= 64 rows
-    ("large only", 5, 300, 128, 3),           # every expert > 64 rows, ragged N
+    ("small only", 17, 768, 384, 2),          # every expert <= 64 rows (64-column tiles)
+    ("small only, 128 wide", 40, 700, 256, 7),  # 40 x 11 > 256 >= 40 x 6: 128-column tiles, ragged N
+    ("small only, 256 wide", 100, 384, 128, 8),  # 100 x 3 > 256: 64 x 256 tiles
+    ("large only", 5, 300, 128, 3),           # every expert > 64 rows, ragged N (128 x 128 tiles)
+    ("large only, 256 tiles", 20, 1300, 128, 9),  # enough rows for 256 x 256 tiles, ragged N
     ("one row", 1, 256, 128, 4),
     ("few tiles", 9, 256, 128, 5),            # fewer tiles than XCDs in a class
     ("m tile boundaries", 12, 384, 256, 6),   # large m tiles of 1, 128, 129 and 256 rows
@@ -360,16 +363,18 @@ def _moe_operands_from_counts(counts, N, K, seed):
 def test_moe_schedule(name, E, N, K, seed):
     """The one-launch schedule of both expert classes (tiles of each class
     cut into eight contiguous parts, the large tiles spread over the first
-    positions of each part): every expert's rows are computed exactly once,
+    positions of each part; small-expert tiles 64, 128 or 256 columns wide
+    and large-expert tiles 128 or 256 square, by the problem size): every
+    expert's rows are computed exactly once,
     compared in full with the oracle on float32 and bf16 outputs; rows no
     expert owns stay untouched."""
     rng = np.random.default_rng(seed)
     if name.startswith("mixed"):
         counts = np.where(rng.random(E) < 0.15, rng.integers(65, 700, E),
                           np.where(rng.random(E) < 0.2, 0, rng.integers(1, 65, E)))
-    elif name == "small only":
+    elif name.startswith("small only"):
         counts = rng.integers(1, 65, E)
-    elif name == "large only":
+    elif name.startswith("large only"):
         counts = rng.integers(65, 700, E)
     elif name == "one row":
         counts = np.array([1])
