@@ -380,6 +380,142 @@ mla_value_kernel(MlaParams p) {
   iter(ntiles - 1, false);
 }
 
+// Value side at decode sizes (T <= 64): a workgroup of NS waves owns one
+// head, 32 value columns d0 .. d0+31 and the token chunk, and wave w takes
+// the latent slices w RK/NS .. (w+1) RK/NS - 1 of the contraction.  With one
+// wave per 32 columns (the kernel above on one-wave workgroups, as this size
+// ran before), 128 heads gave 512 waves that each loaded 16 KB of weight
+// before any compute; here four (two) times as many waves each wait for a
+// quarter (half) of that.  The x tile is shared through LDS as in the kernel
+// above.  After each
+// token tile's MFMAs the waves' partial sums meet in LDS, and after the
+// tile's barrier wave 0 adds them in wave order and writes the 16 x 32
+// result (bf16: staged in LDS and stored as whole 64-byte rows).  Same box,
+// 128 heads, R = 512, bf16 out, graph-replayed, us (one-wave kernel -> this):
+// 32 tokens 5.82-5.93 -> 4.31-4.47, 64 tokens 7.96-7.99 -> 5.70-5.75,
+// 1 token 4.50-4.52 -> 3.51-3.52; eight waves of one slice each: 4.68 at 32
+// tokens.  (The key side split the same way over its d rows ran slower,
+// 4.04 -> 5.93 us at 32 tokens: its 16 x 64 result per tile is four times
+// the partial sums to meet in LDS, and one wave to write out.)
+// ---------------------------------------------------------------------------
+template <int RK, int NS, bool OUT_F32>
+__global__ void __launch_bounds__(64 * NS) mla_value_split_kernel(MlaParams p) {
+  constexpr int CPR = RK * 8;                       // 16-byte chunks per x row (R / 8)
+  constexpr int ROW_BYTES = CPR * 16;
+  constexpr int TILE_BYTES = 16 * ROW_BYTES;
+  constexpr int NL = 16 * CPR / (64 * NS);          // 16-byte loads per lane per tile
+  constexpr int SPW = RK / NS;                      // latent slices per wave
+  static_assert(RK % NS == 0 && 16 * CPR % (64 * NS) == 0, "split");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) v4f red[2][NS][2][64];
+  __shared__ __attribute__((aligned(16))) uint8_t os[2][OUT_F32 ? 16 : 16 * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int wave = threadIdx.x >> 6;
+  const int d0 = blockIdx.y * 32;                   // dv % 32 == 0: every column is real
+  const int h = blockIdx.x % p.H;
+  const int t_begin = (blockIdx.x / p.H) * p.tch;
+  const int t_end = min(p.T, t_begin + p.tch);
+  const int ntiles = (t_end - t_begin + 15) / 16;
+  const int vrow0 = h * (p.dn + p.dv) + p.dn + d0;
+  const int s0 = wave * SPW;
+
+  auto load_tile = [&](int tile, v4u (&xr)[NL]) {
+    const int t0 = t_begin + 16 * tile;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = threadIdx.x + 64 * NS * i;
+      const int tl = min(t0 + q / CPR, t_end - 1);
+      xr[i] = *reinterpret_cast<const v4u*>(p.in + (size_t)tl * p.ld_t + (size_t)h * p.ld_h + 8 * (q % CPR));
+    }
+  };
+  auto store_tile = [&](int b, const v4u (&xr)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = threadIdx.x + 64 * NS * i;
+      const int r = q / CPR, c = q % CPR;
+      *reinterpret_cast<v4u*>(&xs[b][r * ROW_BYTES + ((c ^ r) << 4)]) = xr[i];
+    }
+  };
+
+  v4u xr[NL];
+  load_tile(0, xr);
+
+  v8bf wf[2][SPW][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const uint8_t* base = p.w + (size_t)(vrow0 + 16 * ct + j) * p.R + 16 * g;
+    const float* sc = p.ws + (size_t)(vrow0 >> 7) * (p.R >> 7);
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int s = s0 + u;
+      const v4u wv = *reinterpret_cast<const v4u*>(base + 64 * s);
+      const float scale = sc[s >> 1];
+      wf[ct][u][0] = dequant8_bf16(wv.x, wv.y, scale);
+      wf[ct][u][1] = dequant8_bf16(wv.z, wv.w, scale);
+    }
+  }
+
+  store_tile(0, xr);
+  load_tile(min(1, ntiles - 1), xr);
+  __syncthreads();
+
+  auto iter = [&](int i, bool next) {
+    const int b = i & 1;
+    const uint8_t* row = xs[b] + j * ROW_BYTES;
+    v4f acc[2][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[ct][0] = acc[ct][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = 8 * (s0 + u) + 2 * g + k;
+        const v8bf xf = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(row + ((c ^ j) << 4)));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[ct][k] = mfma_bf16(wf[ct][u][k], xf, acc[ct][k]);
+      }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) red[b][wave][ct][lane] = acc[ct][0] + acc[ct][1];
+    if (next) {
+      store_tile(b ^ 1, xr);
+      load_tile(min(i + 2, ntiles - 1), xr);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int ts = min(t_begin + 16 * i + j, t_end - 1);   // rows past the end: the last row's result
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        v4f v = red[b][0][ct][lane];
+#pragma unroll
+        for (int w = 1; w < NS; ++w) v += red[b][w][ct][lane];
+        if (OUT_F32) {
+          const size_t o = ((size_t)ts * p.H + h) * p.dv + d0 + 16 * ct + 4 * g;
+          *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + o) = v;
+        } else {
+          // columns 16 ct + 4 g .. + 3: half g & 1 of chunk 2 ct + (g >> 1) of row j
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          const int c = 2 * ct + (g >> 1);
+          *reinterpret_cast<v2u*>(&os[b][j * 64 + ((c ^ (j & 3)) << 4) + 8 * (g & 1)]) =
+              v2u{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+        }
+      }
+      if (!OUT_F32) {
+        // the wave's own LDS writes above are complete before its reads
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        const int r = lane >> 2, ch = lane & 3;
+        const int tr = min(t_begin + 16 * i + r, t_end - 1);
+        const v4u v = *reinterpret_cast<const v4u*>(&os[b][r * 64 + ((ch ^ (r & 3)) << 4)]);
+        *reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(p.out) + ((size_t)tr * p.H + h) * p.dv + d0 + 8 * ch) = v;
+      }
+    }
+  };
+  for (int i = 0; i + 1 < ntiles; ++i) iter(i, true);
+  iter(ntiles - 1, false);
+}
+
 // Token chunking, evenly split, a multiple of 16: the largest chunk of 1024,
 // 512 or 256 tokens that still gives at least 512 workgroups (two per CU)
 // over the heads, else 256.  Longer chunks load each head's weight fewer
@@ -446,13 +582,15 @@ hipError_t launch_mla_absorb_value(const void* x, int64_t ld_t, int64_t ld_h, co
   MlaParams p{static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w), ws, out, (int)T,
               (int)H, (int)dn, (int)dv, (int)R, (int)ld_t, (int)ld_h, 0, 0};
   chunk_tokens(p);
-  // one wave per workgroup when few tokens (more workgroups to spread the
-  // weight over the CUs); four (one head's 128 value columns) otherwise, so
-  // the waves that use the same x rows share them through LDS
+  // at most 64 tokens: the latent split over two or four waves of a
+  // workgroup per 32 value columns (mla_value_split_kernel); otherwise four
+  // waves (one head's 128 value columns), so the waves that use the same x
+  // rows share them through LDS
   const bool wide = T > 64;
+  const int ns = (R / 64) % 4 == 0 ? 4 : 2;
   const int waves = wide ? 4 : 1;
   const dim3 grid((unsigned)(H * p.n_tch), (unsigned)((dv / 32 + waves - 1) / waves));
-  const dim3 block(64 * waves);
+  const dim3 block(64 * (wide ? waves : ns));
   // x is the launch's large stream
   const bool nt = T * H * R * 2 >= kStreamBytes;
 #define FP8BS_MLA_V4(RK_, F32_)                                                                     \
@@ -467,8 +605,9 @@ hipError_t launch_mla_absorb_value(const void* x, int64_t ld_t, int64_t ld_h, co
         FP8BS_MLA_V4(RK_, false)                                                                    \
       }                                                                                             \
     } else {                                                                                        \
-      if (out_f32) hipLaunchKernelGGL((mla_value_kernel<RK_, 1, true, false>), grid, block, 0, stream, p); \
-      else hipLaunchKernelGGL((mla_value_kernel<RK_, 1, false, false>), grid, block, 0, stream, p); \
+      constexpr int NS_ = RK_ % 4 == 0 ? 4 : 2;                                                   \
+      if (out_f32) hipLaunchKernelGGL((mla_value_split_kernel<RK_, NS_, true>), grid, block, 0, stream, p); \
+      else hipLaunchKernelGGL((mla_value_split_kernel<RK_, NS_, false>), grid, block, 0, stream, p); \
     }                                                                                               \
     break;
   switch (R / 64) {
