@@ -397,6 +397,26 @@ def test_moe_schedule(name, E, N, K, seed):
         assert np.all(np.isnan(got[R:])), "rows past R written"
 
 
+@pytest.mark.parametrize("counts,N,K", [
+    ([16] * 8, 2048, 7168),                  # 64 x 64 small-expert tiles, 56 K blocks
+    ([16] * 16, 2048, 7168),                 # 64 x 128 small-expert tiles
+    ([150] * 4, 2048, 7168),                 # 128 x 128 large-expert tiles, a 22-row remainder
+    ([64, 64], 7168, 2048),                  # 64 x 64 tiles on the down projection's shape
+    ([0, 16, 200, 64, 65, 3], 2048, 7168),   # both classes on their narrow tiles
+])
+def test_moe_few_experts_full_k(counts, N, K):
+    """Few experts at the workload's N and K: the narrow tiles the launch picks
+    when 256-wide tiles would leave CUs idle run their whole K loop (their
+    stage rings wrap many times); every output against the oracle."""
+    a, a_s, b, b_s, off = _moe_operands_from_counts(np.array(counts, np.int64), N, K, 7100 + len(counts))
+    R = int(off[-1])
+    ref = oracle.moe_gemm(a, a_s, b, b_s, off)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        got = run_moe(a, a_s, b, b_s, off, out_dtype)
+        assert got.shape == (R, N)
+        assert_close(got, ref, f"moe few experts {counts} {out_dtype}")
+
+
 @pytest.mark.parametrize("proj", ["up", "down"])
 def test_moe_full_size(proj):
     """The grouped MoE workload: 4096 tokens, 256 experts, top-8 Zipf(1.1)
