@@ -1485,8 +1485,9 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   // weight stream spreads over more CUs in one round.  A narrow tile streams
   // less per CU than a 64 x 256 one (its fixed per-K-block cost is spread
   // over fewer bytes), so it pays only when it needs no second round:
-  // 8 experts x 16 rows, N = 2048, K = 7168: 57.0 -> 36.4 us with 64-column
-  // tiles, while 31 experts went 78.8 -> 139.3 us when they took four rounds.
+  // 8 experts x 16 rows, N = 2048, K = 7168: 56.6 -> 38.4 us with 64-column
+  // tiles, 16 experts 67.1 -> 44.2 us with 128-column ones, while 31 experts
+  // on 64-column tiles (four rounds) went 78.8 -> 139.3 us.
   const int64_t cus = device_cus();
   p.small_bn = E * ((N + 63) / 64) <= cus ? 64 : E * ((N + 127) / 128) <= cus ? 128 : 256;
   const int64_t nns = (N + p.small_bn - 1) / p.small_bn;
