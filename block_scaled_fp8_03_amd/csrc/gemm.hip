@@ -1499,8 +1499,11 @@ hipError_t launch_moe_gemm(const void* a, const float* a_s, const void* b, const
   // two rounds of them (N = 2048, K = 7168, us: 8 experts x 200 rows 90.8 ->
   // 53.2, 4 x 300 88.4 -> 45.9, 16 x 100 71.4 -> 55.1), else 256 x 256: with
   // more 128 x 128 rounds the narrower tiles lose (12 x 300 94.9 -> 117.9,
-  // 8 x 700 97.2 -> 130.9).
-  p.large_sh = (R / 128 + nlarge) * ((N + 127) / 128) <= 2 * cus ? 7 : 8;
+  // 8 x 700 97.2 -> 130.9).  Below K = 4096 a tile's fixed cost weighs more
+  // against its K loop and only one round is allowed (N = 7168, K = 2048:
+  // 1 x 1000 rows 32.8 -> 35.1 and 2 x 500 31.8 -> 33.8 us with two).
+  const int64_t rounds = K >= 4096 ? 2 : 1;
+  p.large_sh = (R / 128 + nlarge) * ((N + 127) / 128) <= rounds * cus ? 7 : 8;
   const int64_t ml = (R >> p.large_sh) + nlarge;
   p.num_n = (int)((N + (1 << p.large_sh) - 1) >> p.large_sh);
   const int64_t ms = std::min<int64_t>(E, R);
