@@ -518,7 +518,7 @@ __global__ void __launch_bounds__(64 * NS) mla_value_split_kernel(MlaParams p) {
 
 // Token chunking, evenly split, a multiple of 16: the largest chunk of 1024,
 // 512 or 256 tokens that still gives at least 512 workgroups (two per CU)
-// over the heads, else 256.  Longer chunks load each head's weight fewer
+// over the heads, else 256, or less when even that leaves CUs idle (below).  Longer chunks load each head's weight fewer
 // times (measured, 128 heads: 4096 tokens key 167.3 -> 157.5 us and value
 // 131.4 -> 127.4 us with 1024-token chunks against 256; 2048 tokens value
 // 64.6 -> 62.0 us with 512), but a grid below two workgroups per CU lost
@@ -534,6 +534,14 @@ void chunk_tokens(MlaParams& p) {
       cap = c;
       break;
     }
+  // Fewer 256-token workgroups than CUs: 128- or 64-token chunks, re-reading
+  // the weight per chunk rather than leaving CUs idle (128 heads, us, key /
+  // value: 72 tokens 7.54 / 7.39 -> 6.60 / 6.27, 128 tokens 9.80 / 9.57 ->
+  // 8.19 / 7.34, 256 tokens 14.9 / 14.7 -> 11.2 / 10.7; asking for two
+  // workgroups per CU at every size lost at 384 and 640 tokens, 13.5 -> 15.7
+  // and 20.0 -> 22.6 us on the key side).
+  if (cap == 256 && (int64_t)p.H * ((p.T + 255) / 256) < 256)
+    cap = (int64_t)p.H * ((p.T + 127) / 128) >= 256 ? 128 : 64;
   p.n_tch = std::max(1, (p.T + cap - 1) / cap);
   const int per = (p.T + p.n_tch - 1) / p.n_tch;
   p.tch = (per + 15) / 16 * 16;

@@ -68,6 +68,16 @@ def test_mla_small(T, H, dn, dv, R):
     both_sides(T, H, dn, dv, R, 610 + T, q, s)
 
 
+@pytest.mark.parametrize("T", [72, 200])
+def test_mla_mid_tokens_all_heads(T):
+    """128 heads at token counts whose 256-token chunks would leave CUs idle:
+    64-token chunks (the weight re-read per chunk, a ragged last chunk at
+    200 tokens), compared in full."""
+    H, dn, dv, R = 128, 128, 128, 512
+    q, s = wkv_b(H, dn, dv, R, 640 + T)
+    both_sides(T, H, dn, dv, R, 650 + T, q, s)
+
+
 def test_mla_strided_inputs():
     """q_nope as the pages slice it: the first dn of each head's dn + 64 query
     values (head stride dn + 64, token stride H (dn + 64)); x as a view with a
