@@ -932,6 +932,138 @@ gemm_decode8_kernel(GemmParams p, int rows) {
 }
 
 // ----------------------------------------------------------------------------
+// Decode kernel for few weight rows (M <= 32): K split over the waves.
+// ----------------------------------------------------------------------------
+// With a small N the streaming kernel above gives each workgroup a few rows
+// and walks all K blocks in one sequence of stages, so its time is that
+// sequence's latency, not its bytes (32 x 1536 x 7168: 16.8 us for 11 MB).
+// Here a workgroup owns 16 weight rows n0 .. n0+15 and its eight waves deal
+// the K blocks round-robin (wave w: K blocks w, w + 8, ...).  A wave loads
+// its operand fragments straight into registers with range-checked buffer
+// loads, two K blocks ahead.  Every load is unconditional: a K block past the
+// end (and rows past N or M) read zeros at an out-of-range offset and add
+// nothing, so the compiler's in-order wait counts keep the next block in
+// flight.  The codes are decoded to bf16 and multiplied on the bf16 MFMA,
+// with one fold per K block, as in the kernel above (same fragment and K
+// mapping: lane (r16, g) holds bytes 32g .. 32g + 31 of its row's block); the
+// eight waves' sums meet in LDS and wave 0 adds them in wave order.
+template <int MT, bool OUT_F32>
+__global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
+  constexpr int NW = 8;
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int M = p.rows, N = p.N, K = p.K, nkb = K / 128;
+  const int n0 = blockIdx.x * 16;
+  const int nbn = (N + 127) / 128;
+  const uint32_t bad = 0xF0000000u;                      // out of every range: zeros
+  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a), (short)0, (int)(uint32_t)((int64_t)M * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.b), (short)0, (int)(uint32_t)((int64_t)N * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t as_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.a_s), (short)0, (int)(uint32_t)((int64_t)M * nkb * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bs_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.b_s), (short)0, (int)(uint32_t)((int64_t)nbn * nkb * 4), 0x00020000);
+  const uint32_t b_row = (uint32_t)(n0 + r16) * K + 32 * g;
+  uint32_t a_row[MT], as_row[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    a_row[t] = (uint32_t)(16 * t + r16) * K + 32 * g;
+    as_row[t] = (uint32_t)(16 * t + r16) * nkb * 4;
+  }
+  const uint32_t bs_row = (uint32_t)(n0 / 128) * nkb * 4;  // the 16 rows lie in one block row
+
+  struct Frag {
+    u4 b[2];
+    u4 a[MT][2];
+    float as[MT];
+    float bs;
+  };
+  auto load = [&](Frag& f, int kb) {
+    const bool ok = kb < nkb;                              // wave-uniform
+    const uint32_t ko = (uint32_t)kb * 128;
+    f.b[0] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, ok ? b_row + ko : bad, 0, kNonTemporal));
+    f.b[1] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, ok ? b_row + ko + 16 : bad, 0, kNonTemporal));
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      f.a[t][0] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok ? a_row[t] + ko : bad, 0, 0));
+      f.a[t][1] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok ? a_row[t] + ko + 16 : bad, 0, 0));
+      f.as[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(as_rs, ok ? as_row[t] + 4 * kb : bad, 0, 0));
+    }
+    f.bs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs_rs, ok ? bs_row + 4 * kb : bad, 0, 0));
+  };
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const Frag& f) {
+    v8bf bf[4];
+    bf[0] = e4m3x8_to_bf16(f.b[0].x, f.b[0].y);
+    bf[1] = e4m3x8_to_bf16(f.b[0].z, f.b[0].w);
+    bf[2] = e4m3x8_to_bf16(f.b[1].x, f.b[1].y);
+    bf[3] = e4m3x8_to_bf16(f.b[1].z, f.b[1].w);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      v4f pr = {0.0f, 0.0f, 0.0f, 0.0f};
+      pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[0], e4m3x8_to_bf16(f.a[t][0].x, f.a[t][0].y), pr, 0, 0, 0);
+      pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[1], e4m3x8_to_bf16(f.a[t][0].z, f.a[t][0].w), pr, 0, 0, 0);
+      pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[2], e4m3x8_to_bf16(f.a[t][1].x, f.a[t][1].y), pr, 0, 0, 0);
+      pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[3], e4m3x8_to_bf16(f.a[t][1].z, f.a[t][1].w), pr, 0, 0, 0);
+      const float sc = f.as[t] * f.bs;
+      acc[t][0] = __builtin_fmaf(pr[0], sc, acc[t][0]);
+      acc[t][1] = __builtin_fmaf(pr[1], sc, acc[t][1]);
+      acc[t][2] = __builtin_fmaf(pr[2], sc, acc[t][2]);
+      acc[t][3] = __builtin_fmaf(pr[3], sc, acc[t][3]);
+    }
+  };
+  // K blocks per wave, rounded up to whole pairs (uniform; the extra ones are zeros)
+  const int iters = 2 * ((nkb + 2 * NW - 1) / (2 * NW));
+  Frag f0, f1;
+  load(f0, wave);
+  load(f1, wave + NW);
+  for (int it = 0; it < iters; it += 2) {
+    compute(f0);
+    load(f0, wave + NW * (it + 2));
+    compute(f1);
+    load(f1, wave + NW * (it + 3));
+  }
+
+  __shared__ float red[NW][MT * 4][64];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t * 4 + r][lane] = acc[t][r];
+  __syncthreads();
+  if (wave != 0) return;
+  const int n = n0 + 4 * g;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + r16;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = red[0][t * 4 + r][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v[r] += red[w][t * 4 + r][lane];
+    }
+    if (m >= M || n >= N) continue;
+    if (OUT_F32) {
+      float* cp = (float*)p.c + (int64_t)m * N + n;
+      if ((N % 4) == 0 && n + 3 < N) *(float4*)cp = make_float4(v[0], v[1], v[2], v[3]);
+      else for (int r = 0; r < 4; ++r) if (n + r < N) cp[r] = v[r];
+    } else {
+      uint16_t* cp = (uint16_t*)p.c + (int64_t)m * N + n;
+      const uint32_t lo = pack2_bf16(v[0], v[1]), hi = pack2_bf16(v[2], v[3]);
+      if ((N % 4) == 0 && n + 3 < N) *(uint2*)cp = make_uint2(lo, hi);
+      else {
+        const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+        for (int r = 0; r < 4; ++r) if (n + r < N) cp[r] = h[r];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Decode kernel of the BF16 path (W8A16, M <= 32), eight waves.
 // ----------------------------------------------------------------------------
 // The streaming structure of gemm_decode8_kernel with the BF16 path's
@@ -1336,11 +1468,26 @@ int device_cus() {
   return cached[dev];
 }
 
+// Decode GEMMs with N up to this take the split-K kernel.  Same box, us,
+// streaming kernel -> split-K kernel, K = 7168: N = 1536 at M = 1 / 16 / 32
+// 13.7 / 13.9 / 17.5 -> 7.2 / 10.8 / 16.0, N = 576 13.4 / 13.5 / 17.3 -> 7.5 /
+// 11.1 / 16.1, N = 4096 13.6 / 13.8 / 17.8 -> 9.6 / 12.0 / 16.5; 1 x 1536 x
+// 2048 5.8 -> 4.2.  Above it the streaming kernel wins (7168 x 16384 at
+// M = 32: 39 us against 61; 18432 x 7168: 26 against 72).  Four K blocks in
+// flight per wave, or sixteen waves per workgroup, ran 0.3 - 1.5 us slower.
+constexpr int kSplitkMaxN = 4096;
+
 template <int MT>
 hipError_t run_decode(const GemmParams& p, bool out_f32, hipStream_t stream) {
   const int cus = device_cus();
   const int groups = (p.N + 7) / 8;
   if constexpr (MT <= 2) {
+    if (p.N <= kSplitkMaxN) {
+      const int grid = (p.N + 15) / 16;
+      if (out_f32) gemm_decode_splitk_kernel<MT, true><<<dim3(grid), dim3(512), 0, stream>>>(p);
+      else gemm_decode_splitk_kernel<MT, false><<<dim3(grid), dim3(512), 0, stream>>>(p);
+      return hipGetLastError();
+    }
     // eight-wave kernel: rows per workgroup a multiple of 8, at most 72
     const int rows = 8 * std::min(kDecode8Rows / 8, (groups + cus - 1) / cus);
     const int grid = (p.N + rows - 1) / rows;

@@ -102,12 +102,19 @@ def test_gemm_unaligned_scales():
 @pytest.mark.parametrize("M,N,K,unaligned", [
     (32, 18432, 1536, False),   # eight-wave decode kernel, a_s rows as 16-byte loads
     (32, 18432, 1536, True),    # the same with a_s 4 bytes past a 16-byte boundary (column loads)
-    (20, 1000, 640, False),     # K/128 = 5: a partial last stage, column loads, 8 rows per workgroup
-    (9, 2050, 7168, True),      # one 16-row activation tile, ragged N, unaligned a_s
-    (32, 130, 512, False),      # two weight blocks in one workgroup, ragged
+    (20, 4500, 640, False),     # K/128 = 5: a partial last stage, column loads, 24 rows per workgroup
+    (9, 4098, 7168, True),      # one 16-row activation tile, ragged N, unaligned a_s
+    # N <= 4096: the split-K kernel (16 rows per workgroup, K blocks dealt to eight waves)
+    (32, 1536, 7168, False),
+    (1, 576, 7168, True),       # one token, unaligned a_s
+    (20, 1000, 640, False),     # five K blocks for eight waves
+    (9, 2050, 7168, True),      # one 16-row activation tile, ragged N
+    (32, 130, 512, False),      # ragged last workgroup
+    (17, 4096, 2048, False),    # the largest N it takes
 ])
 def test_gemm_decode_paths(M, N, K, unaligned):
-    """The decode kernel (M <= 32) on each of its code paths, compared in full
+    """The decode kernels (M <= 32: the streaming kernel, and the split-K
+    kernel for N <= 4096) on each of their code paths, compared in full
     (outlier activations as in the decode workload)."""
     a, a_s, b, b_s = rand_operands(M, N, K, 6100 + M + N + K, outliers=True)
     ref = oracle.gemm(a, a_s, b, b_s)
