@@ -947,7 +947,10 @@ gemm_decode8_kernel(GemmParams p, int rows) {
 // with one fold per K block, as in the kernel above (same fragment and K
 // mapping: lane (r16, g) holds bytes 32g .. 32g + 31 of its row's block); the
 // eight waves' sums meet in LDS and wave 0 adds them in wave order.
-template <int MT, bool OUT_F32>
+// BF16X: the BF16 path (W8A16): x is bf16 (p.a, no a_s), each weight code is
+// dequantised with its block scale (weight_dequant's rounding) and the
+// products accumulate with no fold, as in w8a16_decode8_kernel.
+template <int MT, bool OUT_F32, bool BF16X = false>
 __global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
   constexpr int NW = 8;
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -957,8 +960,9 @@ __global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
   const int n0 = blockIdx.x * 16;
   const int nbn = (N + 127) / 128;
   const uint32_t bad = 0xF0000000u;                      // out of every range: zeros
+  constexpr int XB = BF16X ? 2 : 1;                      // bytes per activation element
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.a), (short)0, (int)(uint32_t)((int64_t)M * K), 0x00020000);
+      const_cast<uint8_t*>(p.a), (short)0, (int)(uint32_t)((int64_t)M * K * XB), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.b), (short)0, (int)(uint32_t)((int64_t)N * K), 0x00020000);
   const __amdgpu_buffer_rsrc_t as_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -969,14 +973,15 @@ __global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
   uint32_t a_row[MT], as_row[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    a_row[t] = (uint32_t)(16 * t + r16) * K + 32 * g;
+    a_row[t] = (uint32_t)(16 * t + r16) * K * XB + 32 * XB * g;
     as_row[t] = (uint32_t)(16 * t + r16) * nkb * 4;
   }
   const uint32_t bs_row = (uint32_t)(n0 / 128) * nkb * 4;  // the 16 rows lie in one block row
 
+  constexpr int NA = 2 * XB;                             // 16-byte activation loads per row
   struct Frag {
     u4 b[2];
-    u4 a[MT][2];
+    u4 a[MT][NA];
     float as[MT];
     float bs;
   };
@@ -987,9 +992,12 @@ __global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
     f.b[1] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, ok ? b_row + ko + 16 : bad, 0, kNonTemporal));
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      f.a[t][0] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok ? a_row[t] + ko : bad, 0, 0));
-      f.a[t][1] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok ? a_row[t] + ko + 16 : bad, 0, 0));
-      f.as[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(as_rs, ok ? as_row[t] + 4 * kb : bad, 0, 0));
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        f.a[t][i] = __builtin_bit_cast(
+            u4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok ? a_row[t] + XB * ko + 16 * i : bad, 0, 0));
+      if constexpr (!BF16X)
+        f.as[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(as_rs, ok ? as_row[t] + 4 * kb : bad, 0, 0));
     }
     f.bs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs_rs, ok ? bs_row + 4 * kb : bad, 0, 0));
   };
@@ -997,6 +1005,20 @@ __global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](const Frag& f) {
+    if constexpr (BF16X) {
+      // lane (r16, g), step i: codes 32g + 8i .. + 8 of its weight row and
+      // the same K range of token 16t + r16 (bytes 64g + 16i of the x row)
+      v8bf bf[4];
+      bf[0] = dequant8_bf16(f.b[0].x, f.b[0].y, f.bs);
+      bf[1] = dequant8_bf16(f.b[0].z, f.b[0].w, f.bs);
+      bf[2] = dequant8_bf16(f.b[1].x, f.b[1].y, f.bs);
+      bf[3] = dequant8_bf16(f.b[1].z, f.b[1].w, f.bs);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], __builtin_bit_cast(v8bf, f.a[t][i]), acc[t], 0, 0, 0);
+    } else {
     v8bf bf[4];
     bf[0] = e4m3x8_to_bf16(f.b[0].x, f.b[0].y);
     bf[1] = e4m3x8_to_bf16(f.b[0].z, f.b[0].w);
@@ -1014,6 +1036,7 @@ __global__ void __launch_bounds__(512) gemm_decode_splitk_kernel(GemmParams p) {
       acc[t][1] = __builtin_fmaf(pr[1], sc, acc[t][1]);
       acc[t][2] = __builtin_fmaf(pr[2], sc, acc[t][2]);
       acc[t][3] = __builtin_fmaf(pr[3], sc, acc[t][3]);
+    }
     }
   };
   // K blocks per wave, rounded up to whole pairs (uniform; the extra ones are zeros)
@@ -1700,6 +1723,22 @@ hipError_t launch_w8a16_gemm(const void* x, const void* w, const float* w_s, voi
   GemmParams p{};
   p.a = (const uint8_t*)x; p.a_s = nullptr; p.b = (const uint8_t*)w; p.b_s = w_s; p.c = c;
   p.offsets = nullptr; p.rows = (int)M; p.N = (int)N; p.K = (int)K; p.E = 0;
+  if (M <= 32 && N <= kSplitkMaxN) {
+    // few weight rows: K split over the waves (gemm_decode_splitk_kernel),
+    // the FP8 path's rule.  Same box, us, streaming -> split-K, K = 7168:
+    // N = 1536 at M = 1 / 16 / 32 21.5 / 21.8 / 24.7 -> 7.8 / 12.6 / 21.1,
+    // N = 4096 22.1 / 22.0 / 24.5 -> 9.7 / 13.6 / 22.6; 1 x 1536 x 2048
+    // 8.0 -> 4.4.
+    const int grid = (int)((N + 15) / 16);
+    if (M <= 16) {
+      if (out_f32) gemm_decode_splitk_kernel<1, true, true><<<dim3(grid), dim3(512), 0, stream>>>(p);
+      else gemm_decode_splitk_kernel<1, false, true><<<dim3(grid), dim3(512), 0, stream>>>(p);
+    } else {
+      if (out_f32) gemm_decode_splitk_kernel<2, true, true><<<dim3(grid), dim3(512), 0, stream>>>(p);
+      else gemm_decode_splitk_kernel<2, false, true><<<dim3(grid), dim3(512), 0, stream>>>(p);
+    }
+    return hipGetLastError();
+  }
   if (M <= 32) {
     // eight-wave streaming kernel: rows per workgroup a multiple of 8, at most 72
     const int cus = device_cus();

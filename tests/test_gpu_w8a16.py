@@ -42,7 +42,9 @@ def check(got, ref, S, bf16, what):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (1, 1, 128), (16, 256, 256), (32, 200, 384),          # 32-row decode tiles
+    (1, 1, 128), (16, 256, 256), (32, 200, 384),          # decode sizes, N <= 4096: split-K kernel
+    (1, 1536, 7168), (17, 576, 2048), (32, 4096, 640),    # split-K: 56 / 16 / 5 K blocks
+    (20, 4500, 384),                                      # decode sizes, N > 4096: streaming kernel
     (48, 300, 384), (64, 129, 256),                       # 64-row decode tiles
     (65, 200, 384), (257, 129, 256), (300, 520, 1024), (513, 300, 640),   # 64-row tiles (few 128 x 128)
     (100, 18000, 256),                                    # 128 x 128 tiles, one per CU (141)
